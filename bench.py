@@ -1,0 +1,210 @@
+"""Benchmark: the action-decoder layer chain on one MI355X.
+
+One step = one decision = the whole hot path once: 18 layers x 10 flow steps of
+(producer -> QKV GEMM -> attention over the 800-token prefix -> O GEMM -> producer ->
+gate|up GEMM + SiLU gate -> down GEMM), M = 50 action rows, hidden 1024, 8 query heads,
+1 KV head, head dim 128, MLP 4096, bf16 weights and GEMM inputs, replayed as one
+hipGraph.  Inputs and weights are synthetic (seeded), resident in HBM before timing.
+
+Prints one JSON line: value = microseconds per action-decoder layer at M = 50 (decision
+time / 180), plus the M = 10 figure, the weight-stream rate, the roofline of the dominant
+kernel (the gate|up GEMM, timed alone with HIP events) and the float64 CPU oracle timed
+on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def chain_weight_bytes(dims, esz):
+    H, F, nh, hd = dims["hidden"], dims["mlp"], dims["n_heads"], dims["head_dim"]
+    per_layer = (H * (nh + 2) * hd + nh * hd * H + H * 2 * F + F * H) * esz
+    return per_layer * dims["layers"]
+
+
+def kv_bytes(dims):
+    return 2 * dims["prefix"] * dims["head_dim"] * 2 * dims["layers"]
+
+
+def time_chain(torch, ch, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        ch.run(stream.cuda_stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ch.run(stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per decision
+
+
+def time_dominant_gemm(torch, frt, device, synth, dims, dtype, reps=64):
+    """The gate|up GEMM of one layer (M x hidden x 2*mlp, SiLU-gate epilogue) timed alone.
+
+    A pool of distinct packed weight copies (>= 1 GiB, 4x the last-level cache) is cycled
+    so every launch streams its weights from HBM.  Returns (mean us per launch, bytes).
+    """
+    M, H, F = dims["M"], dims["hidden"], dims["mlp"]
+    N = 2 * F
+    w = synth.weight_bf16(synth.TEST_SEED, 6, 0, H, N)
+    pk, cs = device.pack_weight(w, dtype, frt.W_GATE_UP)
+    wbytes = pk.numel()
+    ncopy = max(8, int((1 << 30) // wbytes) + 1)
+    pool = [pk.clone() for _ in range(ncopy)]
+    a = device.empty_bytes(frt.frt_operand_bytes(dtype, M, H))
+    a.zero_()
+    out = device.empty_bytes(frt.frt_operand_bytes(dtype, M, F))
+    splits = frt.frt_splitk_choose(M, N, H, dtype)
+    parts = device.empty_f32(splits, M, N) if splits > 1 else None
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        frt.frt_skinny_gemm_splitk(M, N, H, splits, dtype, frt.W_GATE_UP, a, pool[i % ncopy], cs, 1.0,
+                                   parts, 0 if parts is None else parts.numel() * 4, frt.EPI_SILU_GATE_QUANT,
+                                   out, dtype, 1.0, stream=stream.cuda_stream)
+    for i in range(2 * ncopy):
+        launch(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    extra = (N * 4) if cs is not None else 0
+    return us, wbytes + extra, splits
+
+
+def cpu_baseline(synth, dims_full, budget_s=20.0):
+    """The float64 oracle on a bounded sample of the same workload: all 18 layers of the
+    first flow steps, as many steps as fit the budget (at least one)."""
+    import numpy as np
+    from oracle import codec, ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    dims = dict(dims_full)
+    dims["steps"] = 1
+    wl = synth.workload4(dims)
+    ws = [{n: codec.bf16_decode(l[n]) for n in ("qkv", "o", "up", "down")} for l in wl["layers"]]
+    kp = [codec.bf16_decode(l["k_prefix"]) for l in wl["layers"]]
+    vp = [codec.bf16_decode(l["v_prefix"]) for l in wl["layers"]]
+    layers_done = 0
+    t0 = time.perf_counter()
+    h, xp, gp = wl["x0"].astype(np.float64), None, None
+    while True:
+        for l in range(dims["layers"]):
+            h, xp, gp = ref.layer(h, xp, gp, wl["mod"][0, l, 0], wl["mod"][0, l, 1], ws[l], np.ones(4),
+                                  kp[l], vp[l], dims, "bf16", 1e-6)
+            layers_done += 1
+        if time.perf_counter() - t0 >= budget_s / 2 or layers_done >= 4 * dims["layers"]:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=round(dt / layers_done * 1e6, 1), unit="us/layer", cores=int(cores), kind="oracle",
+                sample=f"{layers_done} layer applications (M={dims['M']}, bf16, float64 NumPy) in {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=18)
+    ap.add_argument("--flow-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the single-batch action-decoder chain is a "
+              "one-device latency path (see the design notes on sharding); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from gemm_chains_amd import chain, device, frt
+    frt.lib()
+    torch.cuda.set_device(0)
+
+    results = {}
+    for M in (50, 10):
+        dims = synth.chain_dims(layers=args.layers, steps=args.flow_steps, M=M)
+        log(f"M={M}: generating {dims['layers']}-layer weights and inputs")
+        wl = synth.workload4(dims)
+        packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
+        ch = chain.Chain(dims, packed, use_graph=True)
+        chain.load_workload(ch, wl)
+        torch.cuda.synchronize()
+        log(f"M={M}: {ch.kernel_count()} kernels per decision; timing {args.steps} decisions")
+        ms = time_chain(torch, ch, args.steps, args.warmup)
+        nl = dims["layers"] * dims["steps"]
+        wb = chain_weight_bytes(dims, 2)
+        results[M] = dict(ms=ms, us_layer=ms * 1e3 / nl, kernels=ch.kernel_count(),
+                          weight_gbs=(wb * dims["steps"] + kv_bytes(dims) * dims["steps"]) / (ms * 1e-3) / 1e9,
+                          dims=dims)
+        log(f"M={M}: {ms:.3f} ms/decision, {results[M]['us_layer']:.2f} us/layer, "
+            f"{results[M]['weight_gbs']:.0f} GB/s weights+KV")
+        ch.close()
+        del packed, wl
+        torch.cuda.empty_cache()
+
+    dims50 = results[50]["dims"]
+    us, nbytes, splits = time_dominant_gemm(torch, frt, device, synth, dims50, frt.BF16)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    log(f"dominant kernel (gate|up GEMM {dims50['M']}x{dims50['hidden']}x{2 * dims50['mlp']}, s={splits}): "
+        f"{us:.2f} us, {achieved:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample")
+        cpu = cpu_baseline(synth, dims50)
+
+    r = results[50]
+    line = {
+        "metric": "µs per action-decoder layer at M=10/50; weight-stream HBM GB/s vs peak",
+        "value": round(r["us_layer"], 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/K) bf16 weights, N(0,1) bf16 prefix K/V)",
+        "config": {"workload": "action-decoder chain, 18 layers x 10 flow steps, M=50, hidden 1024, "
+                               "8 q heads / 1 kv head x 128, 800-token prefix, MLP 4096, bf16, hipGraph replay",
+                   "layers": dims50["layers"], "flow_steps": dims50["steps"], "M": 50,
+                   "kernels_per_decision": r["kernels"]},
+        "us_per_layer_m10": round(results[10]["us_layer"], 3),
+        "ms_per_decision_m10": round(results[10]["ms"], 4),
+        "weight_stream_gbs": round(r["weight_gbs"], 1),
+        "weight_stream_frac_of_peak": round(r["weight_gbs"] / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"skinny_gemm gate|up {dims50['M']}x{dims50['hidden']}x{2 * dims50['mlp']} "
+                               f"bf16 s={splits} +SiLU epilogue", "us_per_launch": round(us, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

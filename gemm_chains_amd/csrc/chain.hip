@@ -1,0 +1,394 @@
+// The action-decoder layer chain: layers x flow steps of producer -> GEMM -> consumer
+// kernels over persistent named buffers, captured once into a hipGraph and replayed.
+//
+// Pages: observation-age notes ("思考探索：具身推理加速，先看动作执行时观测有多旧"), section
+// "CUDA Graph 与图化简分别省掉什么" (record the GPU work once, replay it with the same
+// arguments and addresses, new inputs go into agreed buffers, static shapes), section
+// "固定工作负载给了系统优化更多余地" (batch 1, fixed action length: fixed graph and
+// preallocated buffers, kernels chosen for the real shapes), section
+// "静态量化改变了两次矩阵乘之间的工作" (18 layers x 10 denoising steps = 180 passes; the
+// consumer of layer l prepares layer l+1's input with layer l+1's conditioning);
+// FlashRT-PAI abstract ("FlashRT-PAI: Fast Kernels Are Not Fast Pipelines for Physical AI
+// Inference": named buffers that persist across decisions).
+#include "frt_internal.hpp"
+
+#include <string.h>
+#include <new>
+#include <vector>
+
+namespace frt {
+
+enum { SITE_QKV = 0, SITE_O = 1, SITE_UP = 2, SITE_DOWN = 3 };
+enum { MOD_SCALE = 0, MOD_SHIFT = 1, MOD_GATE = 2 };
+
+struct Buf {
+  size_t off = 0, bytes = 0;
+};
+
+struct ChainLayout {
+  int s_qkv = 0, s_o = 0, s_up = 0, s_down = 0;
+  int nqkv = 0, nattn = 0;
+  size_t op_qkv = 0, op_o = 0, op_up = 0, op_down = 0;     // operand bytes
+  size_t pq = 0, po = 0, pu = 0, pd = 0;                   // partial bytes (one copy)
+  Buf x_in, x_out, mod, act, pk, pv, h, a_qkv, a_o, a_up, a_down, p_qkv, p_o, p_up, p_down;
+  Buf d_h_attn, d_h_mlp, d_a_qkv, d_a_o, d_a_up, d_a_down, d_p_qkv, d_p_o, d_p_down, d_qkv;
+  size_t total = 0;
+};
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static int validate_desc(const frt_chain_desc* d) {
+  FRT_CHECK(d, FRT_E_NULL);
+  FRT_CHECK(d->layers >= 1 && d->layers <= 256 && d->steps >= 1 && d->steps <= 1000, FRT_E_SHAPE);
+  FRT_CHECK(is_ab_dtype(d->dtype), FRT_E_DTYPE);
+  const int ks = kstep_of(d->dtype);
+  FRT_CHECK(d->M >= 1 && d->M <= kMaxM, FRT_E_SHAPE);
+  FRT_CHECK(d->hidden >= ks && d->hidden % ks == 0 && d->hidden <= kMaxProducerK, FRT_E_SHAPE);
+  FRT_CHECK(d->head_dim == 128, FRT_E_SHAPE);
+  FRT_CHECK(d->n_heads >= 1 && d->n_heads <= 16 && (d->n_heads * d->head_dim) % ks == 0, FRT_E_SHAPE);
+  FRT_CHECK(d->prefix_len >= 0 && d->prefix_len <= 8192, FRT_E_SHAPE);
+  FRT_CHECK(d->mlp >= ks && d->mlp % ks == 0 && d->mlp % 16 == 0, FRT_E_SHAPE);
+  FRT_CHECK(d->eps >= 0.f && d->eps == d->eps, FRT_E_ARG);
+  const int sp[4] = {d->splits_qkv, d->splits_o, d->splits_up, d->splits_down};
+  for (int s : sp) FRT_CHECK(s == 0 || is_split(s), FRT_E_SPLITK);
+  FRT_CHECK(d->w_qkv && d->w_o && d->w_up && d->w_down, FRT_E_NULL);
+  for (int l = 0; l < d->layers; ++l) {
+    FRT_CHECK(d->w_qkv[l] && d->w_o[l] && d->w_up[l] && d->w_down[l], FRT_E_NULL);
+    FRT_CHECK(aligned16(d->w_qkv[l]) && aligned16(d->w_o[l]) && aligned16(d->w_up[l]) && aligned16(d->w_down[l]),
+              FRT_E_ALIGN);
+  }
+  if (d->dtype == FRT_E4M3) {
+    FRT_CHECK(d->s_qkv && d->s_o && d->s_up && d->s_down, FRT_E_NULL);
+    for (int l = 0; l < d->layers; ++l) {
+      FRT_CHECK(d->s_qkv[l] && d->s_o[l] && d->s_up[l] && d->s_down[l], FRT_E_NULL);
+      FRT_CHECK(aligned16(d->s_qkv[l]) && aligned16(d->s_o[l]) && aligned16(d->s_up[l]) && aligned16(d->s_down[l]),
+                FRT_E_ALIGN);
+    }
+  }
+  return FRT_OK;
+}
+
+static int resolve_split(int s, int M, int N, int K, int dtype) {
+  return s ? s : choose_splits(M, N, K, dtype);
+}
+
+static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
+  const int M = d->M, H = d->hidden, F = d->mlp, dt = d->dtype;
+  L.nqkv = (d->n_heads + 2) * d->head_dim;
+  L.nattn = d->n_heads * d->head_dim;
+  L.s_qkv = resolve_split(d->splits_qkv, M, L.nqkv, H, dt);
+  L.s_o = resolve_split(d->splits_o, M, H, L.nattn, dt);
+  L.s_up = resolve_split(d->splits_up, M, 2 * F, H, dt);
+  L.s_down = resolve_split(d->splits_down, M, H, F, dt);
+  const int ks = kstep_of(dt);
+  FRT_CHECK((H / ks) % L.s_qkv == 0 && (L.nattn / ks) % L.s_o == 0 && (H / ks) % L.s_up == 0 &&
+                (F / ks) % L.s_down == 0,
+            FRT_E_SPLITK);
+  L.op_qkv = frt_operand_bytes(dt, M, H);
+  L.op_o = frt_operand_bytes(dt, M, L.nattn);
+  L.op_up = frt_operand_bytes(dt, M, H);
+  L.op_down = frt_operand_bytes(dt, M, F);
+  L.pq = (size_t)L.s_qkv * M * L.nqkv * 4;
+  L.po = (size_t)L.s_o * M * H * 4;
+  L.pu = L.s_up > 1 ? (size_t)L.s_up * M * 2 * F * 4 : 0;
+  L.pd = (size_t)L.s_down * M * H * 4;
+  const size_t SL = (size_t)d->steps * d->layers;
+  size_t off = 0;
+  auto take = [&](Buf& b, size_t bytes) {
+    b.off = off;
+    b.bytes = bytes;
+    off = align256(off + bytes);
+  };
+  take(L.x_in, (size_t)M * H * 4);
+  take(L.x_out, (size_t)M * H * 4);
+  take(L.mod, SL * 2 * 3 * H * 4);
+  take(L.act, (size_t)d->layers * 4 * 4);
+  take(L.pk, (size_t)d->layers * d->prefix_len * d->head_dim * 2);
+  take(L.pv, (size_t)d->layers * d->prefix_len * d->head_dim * 2);
+  take(L.h, (size_t)M * H * 4);
+  take(L.a_qkv, L.op_qkv);
+  take(L.a_o, L.op_o);
+  take(L.a_up, L.op_up);
+  take(L.a_down, L.op_down);
+  take(L.p_qkv, L.pq);
+  take(L.p_o, L.po);
+  take(L.p_up, L.pu);
+  take(L.p_down, L.pd);
+  if (d->keep_intermediates) {
+    take(L.d_h_attn, SL * M * H * 4);
+    take(L.d_h_mlp, SL * M * H * 4);
+    take(L.d_a_qkv, SL * align256(L.op_qkv));
+    take(L.d_a_o, SL * align256(L.op_o));
+    take(L.d_a_up, SL * align256(L.op_up));
+    take(L.d_a_down, SL * align256(L.op_down));
+    take(L.d_p_qkv, SL * align256(L.pq));
+    take(L.d_p_o, SL * align256(L.po));
+    take(L.d_p_down, SL * align256(L.pd));
+    take(L.d_qkv, SL * align256((size_t)M * L.nqkv * 2));
+  }
+  L.total = off;
+  return FRT_OK;
+}
+
+}  // namespace frt
+
+using namespace frt;
+
+struct frt_chain {
+  frt_chain_desc d;
+  std::vector<const void*> wq, wo, wu, wd;
+  std::vector<const float*> sq, so, su, sd;
+  uint8_t* arena = nullptr;
+  size_t arena_bytes = 0;
+  ChainLayout L;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int kernels = 0;
+};
+
+static uint8_t* at(frt_chain* c, const Buf& b, size_t idx = 0, size_t stride = 0) {
+  return c->arena + b.off + idx * stride;
+}
+
+// Enqueue the whole chain on `s` (eager launches; also what graph capture records).
+static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
+  const frt_chain_desc& d = c->d;
+  const ChainLayout& L = c->L;
+  const int M = d.M, H = d.hidden, F = d.mlp, MB = m_blocks(M);
+  const bool e4 = d.dtype == FRT_E4M3;
+  const bool dbg = d.keep_intermediates != 0;
+  const size_t modsz = (size_t)3 * H;  // floats per (step, layer, sublayer)
+  float* mod = (float*)at(c, L.mod);
+  float* act = (float*)at(c, L.act);
+  auto modp = [&](int k, int l, int sub, int row) { return mod + (((size_t)k * d.layers + l) * 2 + sub) * modsz + (size_t)row * H; };
+  auto actp = [&](int l, int site) -> const float* { return e4 ? act + l * 4 + site : nullptr; };
+  int n = 0;
+
+  const float* h_prev = (const float*)at(c, L.x_in);
+  const float* pdown_prev = nullptr;
+  int kp = -1, lp = -1;
+  for (int k = 0; k < d.steps; ++k) {
+    for (int l = 0; l < d.layers; ++l) {
+      const size_t idx = (size_t)k * d.layers + l;
+      float* h_attn = dbg ? (float*)at(c, L.d_h_attn, idx, (size_t)M * H * 4) : (float*)at(c, L.h);
+      float* h_mlp = dbg ? (float*)at(c, L.d_h_mlp, idx, (size_t)M * H * 4) : (float*)at(c, L.h);
+      uint8_t* a_qkv = dbg ? at(c, L.d_a_qkv, idx, align256(L.op_qkv)) : at(c, L.a_qkv);
+      uint8_t* a_o = dbg ? at(c, L.d_a_o, idx, align256(L.op_o)) : at(c, L.a_o);
+      uint8_t* a_up = dbg ? at(c, L.d_a_up, idx, align256(L.op_up)) : at(c, L.a_up);
+      uint8_t* a_down = dbg ? at(c, L.d_a_down, idx, align256(L.op_down)) : at(c, L.a_down);
+      float* p_qkv = dbg ? (float*)at(c, L.d_p_qkv, idx, align256(L.pq)) : (float*)at(c, L.p_qkv);
+      float* p_o = dbg ? (float*)at(c, L.d_p_o, idx, align256(L.po)) : (float*)at(c, L.p_o);
+      float* p_down = dbg ? (float*)at(c, L.d_p_down, idx, align256(L.pd)) : (float*)at(c, L.p_down);
+      uint16_t* qkv_dbg = dbg ? (uint16_t*)at(c, L.d_qkv, idx, align256((size_t)M * L.nqkv * 2)) : nullptr;
+
+      // 1. producer: add the previous layer's MLP output, AdaRMSNorm (attention sublayer)
+      RnqParams a{};
+      a.M = M; a.K = H; a.MB = MB;
+      a.x = pdown_prev; a.x_splits = pdown_prev ? L.s_down : 0;
+      a.x_scale = 1.f; a.x_scale_ptr = pdown_prev ? actp(lp, SITE_DOWN) : nullptr;
+      a.x_colscale = (pdown_prev && e4) ? c->sd[lp] : nullptr;
+      a.residual = h_prev; a.residual_out = h_attn;
+      a.gate = pdown_prev ? modp(kp, lp, 1, MOD_GATE) : nullptr;
+      a.ada_scale = modp(k, l, 0, MOD_SCALE); a.ada_shift = modp(k, l, 0, MOD_SHIFT);
+      a.eps = d.eps; a.out_dtype = d.dtype; a.act_scale = 1.f; a.act_scale_ptr = actp(l, SITE_QKV);
+      a.operand = a_qkv;
+      FRT_HIP(launch_rnq(a, s)); ++n;
+
+      // 2. fused QKV GEMM -> partials
+      GemmParams g{};
+      g.M = M; g.MB = MB; g.ab_dtype = d.dtype; g.layout = FRT_W_PLAIN;
+      g.N = L.nqkv; g.K = H; g.splits = L.s_qkv; g.ksteps_per_split = H / kstep_of(d.dtype) / L.s_qkv;
+      g.a = a_qkv; g.w = (const uint8_t*)c->wq[l]; g.colscale = e4 ? c->sq[l] : nullptr;
+      g.act_scale = 1.f; g.act_scale_ptr = actp(l, SITE_QKV); g.partials = p_qkv; g.epi = FRT_EPI_NONE;
+      FRT_HIP(launch_gemm(g, s)); ++n;
+
+      // 3. attention over the cached prefix -> O-projection operand
+      AttnParams t{};
+      t.M = M; t.MB = MB; t.n_heads = d.n_heads; t.prefix_len = d.prefix_len;
+      t.qkv = p_qkv; t.splits = L.s_qkv; t.act_scale = 1.f; t.act_scale_ptr = actp(l, SITE_QKV);
+      t.colscale = e4 ? c->sq[l] : nullptr;
+      t.k_prefix = (const uint16_t*)at(c, L.pk) + (size_t)l * d.prefix_len * d.head_dim;
+      t.v_prefix = (const uint16_t*)at(c, L.pv) + (size_t)l * d.prefix_len * d.head_dim;
+      t.out_dtype = d.dtype; t.out_scale = 1.f; t.out_scale_ptr = actp(l, SITE_O);
+      t.operand = a_o; t.qkv_out = qkv_dbg;
+      FRT_HIP(launch_attention(t, s)); ++n;
+
+      // 4. O projection -> partials
+      g.N = H; g.K = L.nattn; g.splits = L.s_o; g.ksteps_per_split = L.nattn / kstep_of(d.dtype) / L.s_o;
+      g.a = a_o; g.w = (const uint8_t*)c->wo[l]; g.colscale = e4 ? c->so[l] : nullptr;
+      g.act_scale_ptr = actp(l, SITE_O); g.partials = p_o;
+      FRT_HIP(launch_gemm(g, s)); ++n;
+
+      // 5. producer: gated residual of the attention output, AdaRMSNorm (MLP sublayer)
+      RnqParams b = a;
+      b.x = p_o; b.x_splits = L.s_o; b.x_scale_ptr = actp(l, SITE_O);
+      b.x_colscale = e4 ? c->so[l] : nullptr;
+      b.residual = h_attn; b.residual_out = h_mlp; b.gate = modp(k, l, 0, MOD_GATE);
+      b.ada_scale = modp(k, l, 1, MOD_SCALE); b.ada_shift = modp(k, l, 1, MOD_SHIFT);
+      b.act_scale_ptr = actp(l, SITE_UP); b.operand = a_up;
+      FRT_HIP(launch_rnq(b, s)); ++n;
+
+      // 6. gate|up GEMM with SiLU(gate)*up + quantise (fused when not split)
+      g.N = 2 * F; g.K = H; g.splits = L.s_up; g.ksteps_per_split = H / kstep_of(d.dtype) / L.s_up;
+      g.layout = FRT_W_GATE_UP; g.a = a_up; g.w = (const uint8_t*)c->wu[l]; g.colscale = e4 ? c->su[l] : nullptr;
+      g.act_scale_ptr = actp(l, SITE_UP);
+      g.out_dtype = d.dtype; g.out_scale = 1.f; g.out_scale_ptr = actp(l, SITE_DOWN);
+      if (L.s_up == 1) {
+        g.epi = FRT_EPI_SILU_GATE_QUANT; g.out = a_down; g.partials = nullptr;
+        FRT_HIP(launch_gemm(g, s)); ++n;
+      } else {
+        g.epi = FRT_EPI_NONE; g.partials = (float*)at(c, L.p_up);
+        FRT_HIP(launch_gemm(g, s)); ++n;
+        ReduceParams r{};
+        r.M = M; r.N = 2 * F; r.MB = MB; r.splits = L.s_up; r.partials = g.partials;
+        r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_UP); r.colscale = g.colscale;
+        r.epi = FRT_EPI_SILU_GATE_QUANT; r.out = a_down; r.out_dtype = d.dtype; r.out_scale = 1.f;
+        r.out_scale_ptr = actp(l, SITE_DOWN);
+        FRT_HIP(launch_reduce(r, s)); ++n;
+      }
+
+      // 7. down projection -> partials, reduced by the next producer
+      g.N = H; g.K = F; g.splits = L.s_down; g.ksteps_per_split = F / kstep_of(d.dtype) / L.s_down;
+      g.layout = FRT_W_PLAIN; g.a = a_down; g.w = (const uint8_t*)c->wd[l]; g.colscale = e4 ? c->sd[l] : nullptr;
+      g.act_scale_ptr = actp(l, SITE_DOWN); g.epi = FRT_EPI_NONE; g.partials = p_down; g.out = nullptr;
+      FRT_HIP(launch_gemm(g, s)); ++n;
+
+      h_prev = h_mlp;
+      pdown_prev = p_down;
+      kp = k;
+      lp = l;
+    }
+  }
+  // final gated residual of the last MLP output -> x_out
+  RnqParams f{};
+  f.M = M; f.K = H; f.MB = MB; f.x = pdown_prev; f.x_splits = L.s_down; f.x_scale = 1.f;
+  f.x_scale_ptr = actp(lp, SITE_DOWN); f.x_colscale = e4 ? c->sd[lp] : nullptr;
+  f.residual = h_prev; f.residual_out = (float*)at(c, L.x_out); f.gate = modp(kp, lp, 1, MOD_GATE);
+  f.eps = d.eps; f.out_dtype = d.dtype; f.act_scale = 1.f; f.operand = nullptr;
+  FRT_HIP(launch_rnq(f, s)); ++n;
+  if (count) *count = n;
+  return FRT_OK;
+}
+
+extern "C" size_t frt_layer_chain_arena_bytes(const frt_chain_desc* desc) {
+  if (validate_desc(desc) != FRT_OK) return 0;
+  ChainLayout L;
+  if (make_layout(desc, L) != FRT_OK) return 0;
+  return L.total;
+}
+
+extern "C" int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_dev, size_t arena_bytes,
+                                      void* capture_stream, frt_chain** out) {
+  FRT_CHECK(out, FRT_E_NULL);
+  *out = nullptr;
+  int st = validate_desc(desc);
+  if (st) return st;
+  FRT_CHECK(arena_dev, FRT_E_NULL);
+  FRT_CHECK(aligned16(arena_dev), FRT_E_ALIGN);
+  ChainLayout L;
+  st = make_layout(desc, L);
+  if (st) return st;
+  FRT_CHECK(arena_bytes >= L.total, FRT_E_WORKSPACE);
+  frt_chain* c = new (std::nothrow) frt_chain();
+  FRT_CHECK(c, FRT_E_STATE);
+  c->d = *desc;
+  const int nl = desc->layers;
+  c->wq.assign(desc->w_qkv, desc->w_qkv + nl);
+  c->wo.assign(desc->w_o, desc->w_o + nl);
+  c->wu.assign(desc->w_up, desc->w_up + nl);
+  c->wd.assign(desc->w_down, desc->w_down + nl);
+  if (desc->dtype == FRT_E4M3) {
+    c->sq.assign(desc->s_qkv, desc->s_qkv + nl);
+    c->so.assign(desc->s_o, desc->s_o + nl);
+    c->su.assign(desc->s_up, desc->s_up + nl);
+    c->sd.assign(desc->s_down, desc->s_down + nl);
+  } else {
+    c->sq.assign(nl, nullptr); c->so.assign(nl, nullptr); c->su.assign(nl, nullptr); c->sd.assign(nl, nullptr);
+  }
+  c->d.w_qkv = c->wq.data(); c->d.w_o = c->wo.data(); c->d.w_up = c->wu.data(); c->d.w_down = c->wd.data();
+  c->d.s_qkv = c->sq.data(); c->d.s_o = c->so.data(); c->d.s_up = c->su.data(); c->d.s_down = c->sd.data();
+  c->arena = (uint8_t*)arena_dev;
+  c->arena_bytes = arena_bytes;
+  c->L = L;
+  c->kernels = 0;
+  if (desc->use_graph) {
+    hipStream_t cs = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) { set_hip_error((int)e); delete c; return FRT_E_HIP; }
+    if (capture_stream) {
+      // order the capture after whatever the caller already queued
+      hipEvent_t ev;
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess) {
+        (void)hipEventRecord(ev, (hipStream_t)capture_stream);
+        (void)hipStreamWaitEvent(cs, ev, 0);
+        (void)hipEventDestroy(ev);
+      }
+    }
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    int n = 0;
+    int rc = e == hipSuccess ? enqueue_chain(c, cs, &n) : FRT_E_HIP;
+    hipGraph_t g = nullptr;
+    hipError_t e2 = hipStreamEndCapture(cs, &g);
+    if (e != hipSuccess) set_hip_error((int)e);
+    if (rc == FRT_OK && e2 != hipSuccess) { set_hip_error((int)e2); rc = FRT_E_HIP; }
+    if (rc == FRT_OK) {
+      hipError_t e3 = hipGraphInstantiate(&c->exec, g, nullptr, nullptr, 0);
+      if (e3 != hipSuccess) { set_hip_error((int)e3); rc = FRT_E_HIP; }
+    }
+    (void)hipStreamSynchronize(cs);
+    (void)hipStreamDestroy(cs);
+    if (rc != FRT_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      delete c;
+      return rc;
+    }
+    c->graph = g;
+    c->kernels = n;
+  } else {
+    // count the launches without enqueueing anything
+    const int per_layer = c->L.s_up == 1 ? 7 : 8;
+    c->kernels = desc->steps * desc->layers * per_layer + 1;
+  }
+  *out = c;
+  return FRT_OK;
+}
+
+extern "C" int frt_layer_chain_buffer(frt_chain* c, const char* name, void** dev, size_t* bytes) {
+  FRT_CHECK(c && name, FRT_E_STATE);
+  const ChainLayout& L = c->L;
+  struct Named { const char* n; const Buf* b; } tab[] = {
+      {"x_in", &L.x_in}, {"x_out", &L.x_out}, {"mod", &L.mod}, {"act_scale", &L.act},
+      {"prefix_k", &L.pk}, {"prefix_v", &L.pv}, {"h", &L.h},
+      {"dbg_h_attn", &L.d_h_attn}, {"dbg_h_mlp", &L.d_h_mlp}, {"dbg_a_qkv", &L.d_a_qkv},
+      {"dbg_a_o", &L.d_a_o}, {"dbg_a_up", &L.d_a_up}, {"dbg_a_down", &L.d_a_down},
+      {"dbg_p_qkv", &L.d_p_qkv}, {"dbg_p_o", &L.d_p_o}, {"dbg_p_down", &L.d_p_down}, {"dbg_qkv", &L.d_qkv}};
+  for (const Named& t : tab) {
+    if (strcmp(t.n, name) == 0) {
+      if (t.b->bytes == 0) return FRT_E_STATE;
+      if (dev) *dev = c->arena + t.b->off;
+      if (bytes) *bytes = t.b->bytes;
+      return FRT_OK;
+    }
+  }
+  return FRT_E_STATE;
+}
+
+extern "C" int frt_layer_chain_run(frt_chain* c, void* stream) {
+  FRT_CHECK(c, FRT_E_STATE);
+  hipStream_t s = (hipStream_t)stream;
+  if (c->exec) {
+    FRT_HIP(hipGraphLaunch(c->exec, s));
+    return FRT_OK;
+  }
+  return enqueue_chain(c, s, nullptr);
+}
+
+extern "C" int frt_layer_chain_kernel_count(const frt_chain* c) { return c ? c->kernels : -1; }
+
+extern "C" int frt_layer_chain_destroy(frt_chain* c) {
+  FRT_CHECK(c, FRT_E_STATE);
+  if (c->exec) (void)hipGraphExecDestroy(c->exec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  delete c;
+  return FRT_OK;
+}

@@ -1,0 +1,225 @@
+// Internal helpers shared by the kernels and the C ABI of the action-decoder chain.
+// gfx950 (CDNA4) only: wave64, MFMA 16x16x32 bf16 and 16x16x128 f8f6f4.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/frt.h"
+
+namespace frt {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+constexpr int kMaxM = 64;
+constexpr int kMaxSplits = 16;
+constexpr int kMaxProducerK = 4096;
+
+// ------------------------------------------------------------------ status plumbing
+void set_hip_error(int e);
+#define FRT_HIP(call)                                  \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) {                            \
+      frt::set_hip_error((int)e_);                     \
+      return FRT_E_HIP;                                \
+    }                                                  \
+  } while (0)
+#define FRT_CHECK(cond, code) \
+  do {                        \
+    if (!(cond)) return (code); \
+  } while (0)
+
+inline bool aligned16(const void* p) { return (((uintptr_t)p) & 15u) == 0; }
+inline int elem_bytes(int dtype) { return dtype == FRT_BF16 ? 2 : (dtype == FRT_E4M3 ? 1 : 4); }
+inline bool is_ab_dtype(int dtype) { return dtype == FRT_BF16 || dtype == FRT_E4M3; }
+inline bool is_split(int s) { return s == 1 || s == 2 || s == 4 || s == 8 || s == 16; }
+inline int m_blocks(int M) { return (M + 15) / 16; }
+// Elements of K covered by one MFMA k-step (and one packed tile): 32 bf16, 128 e4m3.
+__host__ __device__ inline int kstep_of(int dtype) { return dtype == FRT_BF16 ? 32 : 128; }
+__host__ __device__ inline int tile_bytes_of(int dtype) { return dtype == FRT_BF16 ? 1024 : 2048; }
+inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// ------------------------------------------------------------------ packed layouts
+// Packed GEMM operand (activations), Mp = 16*MB rows, logical A[m][k]:
+//   one tile per (m-block mb, k-step ks) at byte (ks*MB + mb)*TB, so the MB tiles a GEMM
+//   wave needs for one k-step are adjacent.  Inside a tile, MFMA lane L (0..63) owns the
+//   16 bytes at L*16 (bf16) or the two 16-byte halves at h*1024 + L*16 (e4m3), holding
+//   row m = 16*mb + L%16 and k = ks*KS + (L/16)*(KS/4) + [0, KS/4) in increasing order
+//   (KS = 32 or 128); the e4m3 lane's 32 bytes are split into two halves of 16 k each.
+__host__ __device__ inline size_t operand_offset(int dtype, int MB, int m, int k) {
+  const int mb = m >> 4, r = m & 15;
+  if (dtype == FRT_BF16) {
+    const int ks = k >> 5, kk = k & 31;
+    const int lane = r + 16 * (kk >> 3);
+    return ((size_t)ks * MB + mb) * 1024 + (size_t)lane * 16 + (size_t)(kk & 7) * 2;
+  }
+  const int ks = k >> 7, kk = k & 127;
+  const int lane = r + 16 * (kk >> 5);
+  const int half = (kk >> 4) & 1;
+  return ((size_t)ks * MB + mb) * 2048 + (size_t)half * 1024 + (size_t)lane * 16 + (kk & 15);
+}
+
+// Packed weight, logical W[k][n]: the MFMA's A operand is a W^T tile of 16 output
+// columns x one k-step.  Tile (packed column tile pt, k-step ks) sits at byte
+// (pt*KSTEPS + ks)*TB (column-tile major, so a workgroup's share is contiguous); lane L
+// holds column n = 16*lt + L%16 of logical tile lt and the same k positions as above.
+__host__ __device__ inline int packed_tile_of(int layout, int N, int lt) {
+  if (layout == FRT_W_GATE_UP) {
+    const int half_tiles = N / 32;
+    return lt < half_tiles ? 2 * lt : 2 * (lt - half_tiles) + 1;
+  }
+  return lt;
+}
+__host__ __device__ inline int logical_tile_of(int layout, int N, int pt) {
+  if (layout == FRT_W_GATE_UP) return (pt & 1) ? N / 32 + (pt >> 1) : (pt >> 1);
+  return pt;
+}
+__host__ __device__ inline size_t weight_offset(int dtype, int layout, int K, int N, int k, int n) {
+  const int pt = packed_tile_of(layout, N, n >> 4);
+  const int r = n & 15;
+  if (dtype == FRT_BF16) {
+    const int ks = k >> 5, kk = k & 31;
+    const int lane = r + 16 * (kk >> 3);
+    return ((size_t)pt * (K >> 5) + ks) * 1024 + (size_t)lane * 16 + (size_t)(kk & 7) * 2;
+  }
+  const int ks = k >> 7, kk = k & 127;
+  const int lane = r + 16 * (kk >> 5);
+  const int half = (kk >> 4) & 1;
+  return ((size_t)pt * (K >> 7) + ks) * 2048 + (size_t)half * 1024 + (size_t)lane * 16 + (kk & 15);
+}
+
+// ------------------------------------------------------------------ number formats (device)
+// float -> bfloat16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u | ((u >> 16) & 0x8000u);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, (b & 0xffffu) << 16);
+}
+// float -> OCP E4M3FN code: clamp to +-448 first (the hardware convert rounds to
+// nearest even but turns magnitudes past the format into NaN), NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+  if (f != f) return 0x7fu;
+  const float c = fminf(fmaxf(f, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xffu;
+}
+// Four e4m3 codes packed little-endian into one dword.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  const bool nan = (a != a) || (b != b) || (c != c) || (d != d);
+  if (!nan) {
+    const float lo = 448.0f, nlo = -448.0f;
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(a, nlo), lo), fminf(fmaxf(b, nlo), lo), 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(c, nlo), lo), fminf(fmaxf(d, nlo), lo), v, true);
+    return (uint32_t)v;
+  }
+  return e4m3_code(a) | (e4m3_code(b) << 8) | (e4m3_code(c) << 16) | (e4m3_code(d) << 24);
+}
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
+
+// Write 4 consecutive logical k (k % 4 == 0) of row m of a packed operand.
+// e4m3 values are divided by the static activation scale first (correctly rounded).
+__device__ __forceinline__ void store_operand4(uint8_t* op, int dtype, int MB, int m, int k, float v0,
+                                               float v1, float v2, float v3, float scale_e4m3,
+                                               bool zero) {
+  const size_t off = operand_offset(dtype, MB, m, k);
+  if (dtype == FRT_BF16) {
+    u32x2 w;
+    w.x = zero ? 0u : bf16_pack2(v0, v1);
+    w.y = zero ? 0u : bf16_pack2(v2, v3);
+    *reinterpret_cast<u32x2*>(op + off) = w;
+  } else {
+    uint32_t w = zero ? 0u : e4m3_pack4(v0 / scale_e4m3, v1 / scale_e4m3, v2 / scale_e4m3, v3 / scale_e4m3);
+    *reinterpret_cast<uint32_t*>(op + off) = w;
+  }
+}
+
+__device__ __forceinline__ float load_scale(const float* p, float v) { return p ? __ldg(p) : v; }
+
+// ------------------------------------------------------------------ kernel parameter blocks
+struct RnqParams {
+  int M, K, MB;
+  const float* x;            // [splits][M][K] or null
+  int x_splits;
+  float x_scale;
+  const float* x_scale_ptr;  // device scalar overriding x_scale (chain), or null
+  const float* x_colscale;   // [K] or null
+  const float* residual;     // [M][K]
+  float* residual_out;       // [M][K] or null
+  const float* gate;         // [K] or null
+  const float* ada_scale;    // [K] or null
+  const float* ada_shift;    // [K] or null
+  float eps;
+  int out_dtype;
+  float act_scale;
+  const float* act_scale_ptr;
+  uint8_t* operand;          // packed or null
+};
+
+struct GemmParams {
+  int M, N, K, MB, splits;
+  int ab_dtype, layout;
+  int ksteps_per_split;      // K / kstep / splits
+  int kwaves;                // waves per workgroup splitting the chunk
+  const uint8_t* a;
+  const uint8_t* w;
+  const float* colscale;
+  float act_scale;
+  const float* act_scale_ptr;
+  float* partials;           // [splits][M][N] when epi == NONE or splits > 1
+  int epi;                   // epilogue applied in-kernel (only with splits == 1)
+  void* out;
+  int out_dtype;
+  float out_scale;
+  const float* out_scale_ptr;
+};
+
+struct ReduceParams {
+  int M, N, MB, splits;
+  const float* partials;
+  float act_scale;
+  const float* act_scale_ptr;
+  const float* colscale;
+  int epi;
+  void* out;
+  int out_dtype;
+  float out_scale;
+  const float* out_scale_ptr;
+};
+
+struct AttnParams {
+  int M, MB, n_heads, prefix_len;
+  const float* qkv;          // [splits][M][(n_heads+2)*128]
+  int splits;
+  float act_scale;
+  const float* act_scale_ptr;
+  const float* colscale;
+  const uint16_t* k_prefix;  // [prefix_len][128]
+  const uint16_t* v_prefix;
+  int out_dtype;
+  float out_scale;
+  const float* out_scale_ptr;
+  uint8_t* operand;
+  uint16_t* qkv_out;
+};
+
+// Launchers (stream-ordered, no validation: callers validate first).
+hipError_t launch_rnq(const RnqParams& p, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+// Library choices of split count and waves per workgroup.
+int choose_splits(int M, int N, int K, int dtype);
+int choose_kwaves(int ksteps_per_split, int frags);
+
+}  // namespace frt

@@ -1,0 +1,184 @@
+// Offline weight preparation and the host-side layout helpers.
+//
+// Pages: observation-age notes ("思考探索：具身推理加速，先看动作执行时观测有多旧"),
+// section "CUDA Graph 与图化简分别省掉什么" (a fixed per-channel RMSNorm gain folds into the
+// weight, W' = diag(gamma) W; rounding must be checked at low precision), section
+// "静态量化改变了两次矩阵乘之间的工作" (weight scales are kept apart from the GEMM-input
+// activation scales), section "小 M GEMM 要看并行度，也要看归约代价" (the skinny path keeps
+// re-laid-out weight copies).
+#include "frt_internal.hpp"
+
+#include <string.h>
+
+namespace frt {
+
+// s_w[n] = max_k |gamma[k] * W[k][n]| / 448 (fp32), one thread per column; consecutive
+// threads read consecutive columns of a row, so every row read is coalesced.
+__global__ void __launch_bounds__(256) colscale_kernel(const uint16_t* __restrict__ w, const float* __restrict__ gamma,
+                                                       int K, int N, float* __restrict__ colscale) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float amax = 0.f;
+  for (int k = 0; k < K; ++k) {
+    float v = bf16_to_f32(w[(size_t)k * N + n]);
+    if (gamma) v *= gamma[k];
+    amax = fmaxf(amax, fabsf(v));
+  }
+  colscale[n] = amax / 448.0f;
+}
+
+// One thread per 16-byte lane slot of the packed weight.
+__global__ void __launch_bounds__(256) pack_weight_kernel(const uint16_t* __restrict__ w, const float* __restrict__ gamma,
+                                                          int K, int N, int dtype, int layout,
+                                                          const float* __restrict__ colscale, uint8_t* __restrict__ out) {
+  const size_t slot = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nslots = (size_t)K * N * (dtype == FRT_BF16 ? 2 : 1) / 16;
+  if (slot >= nslots) return;
+  const int KSTEP = kstep_of(dtype);
+  const int KS = K / KSTEP;
+  int lane, half = 0;
+  size_t tile;
+  if (dtype == FRT_BF16) {
+    tile = slot / 64;
+    lane = (int)(slot % 64);
+  } else {
+    tile = slot / 128;
+    half = (int)((slot % 128) / 64);
+    lane = (int)(slot % 64);
+  }
+  const int pt = (int)(tile / KS), ks = (int)(tile % KS);
+  const int n = logical_tile_of(layout, N, pt) * 16 + (lane & 15);
+  const int k0 = ks * KSTEP + (lane >> 4) * (KSTEP / 4) + half * 16;
+  u32x4 v;
+  uint32_t* vw = reinterpret_cast<uint32_t*>(&v);
+  if (dtype == FRT_BF16) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float a = bf16_to_f32(w[(size_t)(k0 + e) * N + n]);
+      float b = bf16_to_f32(w[(size_t)(k0 + e + 1) * N + n]);
+      if (gamma) {
+        a *= gamma[k0 + e];
+        b *= gamma[k0 + e + 1];
+      }
+      vw[e / 2] = bf16_pack2(a, b);
+    }
+  } else {
+    const float s = colscale[n];
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      float x[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float a = bf16_to_f32(w[(size_t)(k0 + e + q) * N + n]);
+        if (gamma) a *= gamma[k0 + e + q];
+        x[q] = s > 0.f ? a / s : 0.f;
+      }
+      vw[e / 4] = e4m3_pack4(x[0], x[1], x[2], x[3]);
+    }
+  }
+  *reinterpret_cast<u32x4*>(out + slot * 16) = v;
+}
+
+}  // namespace frt
+
+using namespace frt;
+
+extern "C" size_t frt_operand_bytes(int dtype, int M, int K) {
+  if (!is_ab_dtype(dtype) || M < 1 || M > kMaxM || K < 1) return 0;
+  return (size_t)m_blocks(M) * 16 * K * elem_bytes(dtype);
+}
+
+extern "C" size_t frt_weight_bytes(int dtype, int K, int N) {
+  if (!is_ab_dtype(dtype) || K < 1 || N < 1) return 0;
+  return (size_t)K * N * elem_bytes(dtype);
+}
+
+static int check_operand_shape(int dtype, int M, int K) {
+  FRT_CHECK(is_ab_dtype(dtype), FRT_E_DTYPE);
+  FRT_CHECK(M >= 1 && M <= kMaxM, FRT_E_SHAPE);
+  FRT_CHECK(K >= kstep_of(dtype) && K % kstep_of(dtype) == 0, FRT_E_SHAPE);
+  return FRT_OK;
+}
+
+static int check_weight_shape(int dtype, int K, int N, int layout) {
+  FRT_CHECK(is_ab_dtype(dtype), FRT_E_DTYPE);
+  FRT_CHECK(K >= kstep_of(dtype) && K % kstep_of(dtype) == 0, FRT_E_SHAPE);
+  FRT_CHECK(N >= 16 && N % 16 == 0, FRT_E_SHAPE);
+  FRT_CHECK(layout == FRT_W_PLAIN || layout == FRT_W_GATE_UP, FRT_E_ARG);
+  if (layout == FRT_W_GATE_UP) FRT_CHECK(N % 32 == 0, FRT_E_SHAPE);
+  return FRT_OK;
+}
+
+extern "C" int frt_operand_pack_host(const void* codes_host, int dtype, int M, int K, void* packed_host) {
+  FRT_CHECK(codes_host && packed_host, FRT_E_NULL);
+  int st = check_operand_shape(dtype, M, K);
+  if (st) return st;
+  const int MB = m_blocks(M), esz = elem_bytes(dtype);
+  uint8_t* out = (uint8_t*)packed_host;
+  memset(out, 0, frt_operand_bytes(dtype, M, K));
+  for (int m = 0; m < M; ++m)
+    for (int k = 0; k < K; ++k)
+      memcpy(out + operand_offset(dtype, MB, m, k), (const uint8_t*)codes_host + ((size_t)m * K + k) * esz, esz);
+  return FRT_OK;
+}
+
+extern "C" int frt_operand_unpack_host(const void* packed_host, int dtype, int M, int K, void* codes_host) {
+  FRT_CHECK(codes_host && packed_host, FRT_E_NULL);
+  int st = check_operand_shape(dtype, M, K);
+  if (st) return st;
+  const int MB = m_blocks(M), esz = elem_bytes(dtype);
+  for (int m = 0; m < M; ++m)
+    for (int k = 0; k < K; ++k)
+      memcpy((uint8_t*)codes_host + ((size_t)m * K + k) * esz, (const uint8_t*)packed_host + operand_offset(dtype, MB, m, k), esz);
+  return FRT_OK;
+}
+
+extern "C" int frt_weight_pack_host(const void* codes_host, int dtype, int K, int N, int layout, void* packed_host) {
+  FRT_CHECK(codes_host && packed_host, FRT_E_NULL);
+  int st = check_weight_shape(dtype, K, N, layout);
+  if (st) return st;
+  const int esz = elem_bytes(dtype);
+  for (int k = 0; k < K; ++k)
+    for (int n = 0; n < N; ++n)
+      memcpy((uint8_t*)packed_host + weight_offset(dtype, layout, K, N, k, n),
+             (const uint8_t*)codes_host + ((size_t)k * N + n) * esz, esz);
+  return FRT_OK;
+}
+
+extern "C" int frt_weight_unpack_host(const void* packed_host, int dtype, int K, int N, int layout, void* codes_host) {
+  FRT_CHECK(codes_host && packed_host, FRT_E_NULL);
+  int st = check_weight_shape(dtype, K, N, layout);
+  if (st) return st;
+  const int esz = elem_bytes(dtype);
+  for (int k = 0; k < K; ++k)
+    for (int n = 0; n < N; ++n)
+      memcpy((uint8_t*)codes_host + ((size_t)k * N + n) * esz,
+             (const uint8_t*)packed_host + weight_offset(dtype, layout, K, N, k, n), esz);
+  return FRT_OK;
+}
+
+extern "C" int frt_pack_weight(void* stream, int K, int N, const uint16_t* w_bf16_dev, const float* gamma_dev,
+                               int dtype, int layout, void* w_packed_dev, float* colscale_dev) {
+  FRT_CHECK(w_bf16_dev && w_packed_dev, FRT_E_NULL);
+  int st = check_weight_shape(dtype, K, N, layout);
+  if (st) return st;
+  if (dtype == FRT_E4M3) FRT_CHECK(colscale_dev, FRT_E_NULL);
+  const void* ptrs[] = {w_bf16_dev, gamma_dev, w_packed_dev, dtype == FRT_E4M3 ? colscale_dev : nullptr};
+  for (const void* q : ptrs) FRT_CHECK(aligned16(q), FRT_E_ALIGN);
+  const size_t wb = (size_t)K * N * 2, pb = frt_weight_bytes(dtype, K, N);
+  FRT_CHECK(!overlaps(w_bf16_dev, wb, w_packed_dev, pb), FRT_E_ALIAS);
+  if (dtype == FRT_E4M3) {
+    FRT_CHECK(!overlaps(colscale_dev, (size_t)N * 4, w_packed_dev, pb), FRT_E_ALIAS);
+    FRT_CHECK(!overlaps(colscale_dev, (size_t)N * 4, w_bf16_dev, wb), FRT_E_ALIAS);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == FRT_E4M3) {
+    hipLaunchKernelGGL(colscale_kernel, dim3((N + 255) / 256), dim3(256), 0, s, w_bf16_dev, gamma_dev, K, N, colscale_dev);
+    FRT_HIP(hipGetLastError());
+  }
+  const size_t nslots = pb / 16;
+  hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, w_bf16_dev, gamma_dev,
+                     K, N, dtype, layout, (const float*)colscale_dev, (uint8_t*)w_packed_dev);
+  FRT_HIP(hipGetLastError());
+  return FRT_OK;
+}

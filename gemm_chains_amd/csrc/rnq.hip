@@ -1,0 +1,173 @@
+// Producer: [split-K reduce + scale recovery] -> gated residual -> (Ada)RMSNorm ->
+// static-scale quantisation, written straight into the packed operand of the next GEMM.
+//
+// Pages: observation-age notes ("思考探索：具身推理加速，先看动作执行时观测有多旧"),
+// section "CUDA Graph 与图化简分别省掉什么" (RMSNorm: xhat = x / sqrt(mean(x^2) + eps)),
+// section "静态量化改变了两次矩阵乘之间的工作" (scale fixed ahead of the run; gated residual,
+// AdaRMSNorm and FP8 conversion fused; the consumer of layer l prepares layer l+1's input
+// with layer l+1's conditioning), section "小 M GEMM 要看并行度，也要看归约代价" (the next
+// consumer reduces the FP32 partial sums); rebasdaily FlashRT-PAI news summary, section
+// "它优化的是“接力方式”" (the producer's output layout is exactly what the GEMM reads).
+//
+// One wave64 owns one row: each lane keeps K/64 values in registers (16 per 1024), the
+// sum of squares is reduced with a fixed butterfly (deterministic), and every lane writes
+// whole 16-byte slots of the packed operand.  Four rows per 256-thread workgroup; rows
+// M..Mp-1 write zero codes so the GEMM can always read full 16-row blocks.
+#include "frt_internal.hpp"
+
+namespace frt {
+
+constexpr int kRnqChunks = kMaxProducerK / (64 * 16);  // 16-element chunks per lane, max
+
+__global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int Mp = p.MB * 16;
+  if (m >= Mp) return;
+  const int nchunk = p.K >> 4;  // 16-element chunks in a row
+  if (m >= p.M) {
+    if (p.operand) {
+      for (int c = lane; c < nchunk; c += 64)
+        for (int q = 0; q < 4; ++q)
+          store_operand4(p.operand, p.out_dtype, p.MB, m, c * 16 + 4 * q, 0.f, 0.f, 0.f, 0.f, 1.f, true);
+    }
+    return;
+  }
+  const float xs = load_scale(p.x_scale_ptr, p.x_scale);
+  const size_t row = (size_t)m * p.K;
+  const size_t split_stride = (size_t)p.M * p.K;
+
+  float h[kRnqChunks][16];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRnqChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nchunk) break;
+    const int k0 = c * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 r = *reinterpret_cast<const f32x4*>(p.residual + row + k0 + 4 * q);
+      f32x4 hv = r;
+      if (p.x) {
+        f32x4 x = *reinterpret_cast<const f32x4*>(p.x + row + k0 + 4 * q);
+        for (int j = 1; j < p.x_splits; ++j) {
+          const f32x4 xj = *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0 + 4 * q);
+          x += xj;  // ascending split order
+        }
+        x *= xs;
+        if (p.x_colscale) x *= *reinterpret_cast<const f32x4*>(p.x_colscale + k0 + 4 * q);
+        if (p.gate) x *= *reinterpret_cast<const f32x4*>(p.gate + k0 + 4 * q);
+        hv = r + x;
+      }
+      if (p.residual_out) *reinterpret_cast<f32x4*>(p.residual_out + row + k0 + 4 * q) = hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[i][4 * q + e] = hv[e];
+        ss = fmaf(hv[e], hv[e], ss);
+      }
+    }
+  }
+  if (!p.operand) return;
+  // wave-wide sum of squares, fixed butterfly order
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  const float inv = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+  const float as = load_scale(p.act_scale_ptr, p.act_scale);
+
+#pragma unroll
+  for (int i = 0; i < kRnqChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nchunk) break;
+    const int k0 = c * 16;
+    float y[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, sh = {0.f, 0.f, 0.f, 0.f};
+      if (p.ada_scale) sc = *reinterpret_cast<const f32x4*>(p.ada_scale + k0 + 4 * q);
+      if (p.ada_shift) sh = *reinterpret_cast<const f32x4*>(p.ada_shift + k0 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xh = h[i][4 * q + e] * inv;
+        float v = p.ada_scale ? xh * (1.0f + sc[e]) : xh;
+        if (p.ada_shift) v = v + sh[e];
+        y[4 * q + e] = v;
+      }
+    }
+    if (p.out_dtype == FRT_BF16) {
+      // 16 consecutive k = two 16-byte lane slots of the packed bf16 operand
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        u32x4 w;
+        w.x = bf16_pack2(y[8 * g + 0], y[8 * g + 1]);
+        w.y = bf16_pack2(y[8 * g + 2], y[8 * g + 3]);
+        w.z = bf16_pack2(y[8 * g + 4], y[8 * g + 5]);
+        w.w = bf16_pack2(y[8 * g + 6], y[8 * g + 7]);
+        *reinterpret_cast<u32x4*>(p.operand + operand_offset(FRT_BF16, p.MB, m, k0 + 8 * g)) = w;
+      }
+    } else {
+      // 16 consecutive k (16-aligned) = one 16-byte half slot of the packed e4m3 operand
+      u32x4 w;
+      w.x = e4m3_pack4(y[0] / as, y[1] / as, y[2] / as, y[3] / as);
+      w.y = e4m3_pack4(y[4] / as, y[5] / as, y[6] / as, y[7] / as);
+      w.z = e4m3_pack4(y[8] / as, y[9] / as, y[10] / as, y[11] / as);
+      w.w = e4m3_pack4(y[12] / as, y[13] / as, y[14] / as, y[15] / as);
+      *reinterpret_cast<u32x4*>(p.operand + operand_offset(FRT_E4M3, p.MB, m, k0)) = w;
+    }
+  }
+}
+
+hipError_t launch_rnq(const RnqParams& p, hipStream_t s) {
+  const int Mp = p.MB * 16;
+  const int rows = p.operand ? Mp : p.M;
+  hipLaunchKernelGGL(rnq_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace frt
+
+using namespace frt;
+
+extern "C" int frt_residual_norm_quant(void* stream, int M, int K, const float* x_dev, int x_splits,
+                                       float x_scale, const float* x_colscale_dev,
+                                       const float* residual_dev, float* residual_out_dev,
+                                       const float* gate_dev, const float* ada_scale_dev,
+                                       const float* ada_shift_dev, float eps, int out_dtype,
+                                       float act_scale, void* operand_out_dev) {
+  FRT_CHECK(residual_dev, FRT_E_NULL);
+  FRT_CHECK(operand_out_dev || residual_out_dev, FRT_E_NULL);
+  FRT_CHECK(M >= 1 && M <= kMaxM, FRT_E_SHAPE);
+  FRT_CHECK(K >= 16 && K <= kMaxProducerK && K % 16 == 0, FRT_E_SHAPE);
+  if (operand_out_dev) {
+    FRT_CHECK(is_ab_dtype(out_dtype), FRT_E_DTYPE);
+    FRT_CHECK(K % kstep_of(out_dtype) == 0, FRT_E_SHAPE);
+    if (out_dtype == FRT_E4M3) FRT_CHECK(act_scale > 0.f && act_scale < __builtin_huge_valf(), FRT_E_ARG);
+  }
+  if (x_dev) FRT_CHECK(x_splits >= 1 && x_splits <= kMaxSplits, FRT_E_SPLITK);
+  FRT_CHECK(eps >= 0.f && eps == eps, FRT_E_ARG);
+  const void* ptrs[] = {x_dev, x_colscale_dev, residual_dev, residual_out_dev, gate_dev,
+                        ada_scale_dev, ada_shift_dev, operand_out_dev};
+  for (const void* q : ptrs) FRT_CHECK(aligned16(q), FRT_E_ALIGN);
+  const size_t mk = (size_t)M * K * 4;
+  const size_t opb = operand_out_dev ? frt_operand_bytes(out_dtype, M, K) : 0;
+  // the residual may be updated in place; every other output must stand apart
+  FRT_CHECK(!overlaps(operand_out_dev, opb, residual_dev, mk), FRT_E_ALIAS);
+  FRT_CHECK(!overlaps(operand_out_dev, opb, residual_out_dev, mk), FRT_E_ALIAS);
+  if (x_dev) {
+    const size_t xb = mk * (size_t)x_splits;
+    FRT_CHECK(!overlaps(operand_out_dev, opb, x_dev, xb), FRT_E_ALIAS);
+    FRT_CHECK(!overlaps(residual_out_dev, mk, x_dev, xb), FRT_E_ALIAS);
+  }
+  if (residual_out_dev && residual_out_dev != residual_dev)
+    FRT_CHECK(!overlaps(residual_out_dev, mk, residual_dev, mk), FRT_E_ALIAS);
+
+  RnqParams p{};
+  p.M = M; p.K = K; p.MB = m_blocks(M);
+  p.x = x_dev; p.x_splits = x_dev ? x_splits : 0; p.x_scale = x_scale; p.x_scale_ptr = nullptr;
+  p.x_colscale = x_colscale_dev; p.residual = residual_dev; p.residual_out = residual_out_dev;
+  p.gate = gate_dev; p.ada_scale = ada_scale_dev; p.ada_shift = ada_shift_dev; p.eps = eps;
+  p.out_dtype = operand_out_dev ? out_dtype : FRT_BF16;
+  p.act_scale = out_dtype == FRT_E4M3 ? act_scale : 1.0f; p.act_scale_ptr = nullptr;
+  p.operand = (uint8_t*)operand_out_dev;
+  FRT_HIP(launch_rnq(p, (hipStream_t)stream));
+  return FRT_OK;
+}

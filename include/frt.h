@@ -1,0 +1,257 @@
+/*
+ * frt.h -- C ABI of the MI355X (gfx950) action-decoder layer-chain library.
+ *
+ * The library computes, on one GPU, the hot path the FlashRT-PAI pages describe for
+ * the single-batch action decoder of a flow-matching VLA policy:
+ *
+ *   producer   gated residual add + (Ada)RMSNorm + static-scale quantisation, writing
+ *              the next GEMM's input directly in the tile layout that GEMM reads
+ *              (pages: "思考探索：具身推理加速，先看动作执行时观测有多旧", sections
+ *              "CUDA Graph 与图化简分别省掉什么" -- RMSNorm and W' = diag(gamma) W
+ *              equations -- and "静态量化改变了两次矩阵乘之间的工作"; rebasdaily
+ *              FlashRT-PAI news summary, section "它优化的是“接力方式”": the producer's
+ *              output layout is chosen so the next GEMM reads no extra data);
+ *   GEMM       skinny C = A W with M <= 64 rows, split along K into FP32 partial sums
+ *              (same notes, section "小 M GEMM 要看并行度，也要看归约代价", split-K
+ *              equation);
+ *   consumer   the next kernel reduces the FP32 partials in a fixed order, recovers the
+ *              scales and carries on (norm + quantise, or SiLU gate + quantise);
+ *   chain      layers x flow steps of the above, captured once into a hipGraph over
+ *              persistent named buffers and replayed (same notes, section
+ *              "CUDA Graph 与图化简分别省掉什么": replay reuses arguments and addresses,
+ *              new inputs go into agreed buffers).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers (hipMalloc'd or torch CUDA tensors);
+ *     pointers named *_host are host pointers.  All device pointers must be 16-byte
+ *     aligned.  The library never allocates device memory except the hipGraph objects
+ *     owned by a chain handle; every buffer is owned by the caller.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *     Calls are asynchronous on that stream unless stated otherwise.
+ *   - Every argument is validated before any HIP call: an invalid call returns an
+ *     FRT_E_* code and enqueues nothing.  A failing HIP call returns FRT_E_HIP and its
+ *     hipError_t is kept per thread (frt_last_hip_error).  Nothing aborts and no C++
+ *     exception crosses the ABI.
+ *   - Shapes: 1 <= M <= 64 action rows.  bf16 operands need K % 32 == 0, e4m3 operands
+ *     K % 128 == 0; N % 16 == 0.  M is padded to Mp = 16 * ceil(M / 16) in packed
+ *     operands; padding rows are written as zero codes by every producer.
+ *   - Numbers: bf16 = bfloat16, round to nearest even.  e4m3 = OCP E4M3FN, round to
+ *     nearest even, saturating to +-448, NaN -> 0x7F.
+ */
+#ifndef FRT_H
+#define FRT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FRT_OK = 0,
+  FRT_E_NULL = 1,       /* a required pointer is NULL                                  */
+  FRT_E_SHAPE = 2,      /* M, N, K or another size out of range / not a multiple        */
+  FRT_E_ALIGN = 3,      /* a device pointer is not 16-byte aligned                      */
+  FRT_E_DTYPE = 4,      /* unsupported dtype / dtype combination                        */
+  FRT_E_SPLITK = 5,     /* split count not in {1,2,4,8,16} or K not divisible           */
+  FRT_E_WORKSPACE = 6,  /* a workspace / arena is smaller than required                 */
+  FRT_E_ALIAS = 7,      /* an output overlaps an input it may not overlap               */
+  FRT_E_STATE = 8,      /* handle misuse (NULL handle, unknown buffer name, ...)        */
+  FRT_E_HIP = 9,        /* a HIP runtime call failed; see frt_last_hip_error()          */
+  FRT_E_ARG = 10        /* another invalid argument (epilogue, layout, eps, scale)      */
+} frt_status;
+
+typedef enum { FRT_BF16 = 1, FRT_E4M3 = 2, FRT_F32 = 3 } frt_dtype;
+
+/* Logical column order of a packed weight.  FRT_W_GATE_UP pairs column tile i of the
+ * gate half [0, N/2) with tile i of the up half [N/2, N) so that one workgroup holds
+ * both and can apply SiLU(gate) * up in registers. */
+typedef enum { FRT_W_PLAIN = 0, FRT_W_GATE_UP = 1 } frt_wlayout;
+
+typedef enum {
+  FRT_EPI_NONE = 0,            /* leave [splits][M][N] fp32 partial sums             */
+  FRT_EPI_STORE_F32 = 1,       /* reduce + scale recovery, store [M][N] fp32         */
+  FRT_EPI_STORE_BF16 = 2,      /* reduce + scale recovery, store [M][N] bf16 bits    */
+  FRT_EPI_SILU_GATE_QUANT = 3  /* reduce + scale recovery + SiLU(gate)*up + quantise
+                                  into the packed operand [Mp][N/2] of the next GEMM */
+} frt_epilogue;
+
+/* ------------------------------------------------------------------ diagnostics */
+const char* frt_status_string(int status);
+int frt_last_hip_error(void);      /* hipError_t of this thread's last FRT_E_HIP, else 0 */
+int frt_version(void);             /* 100 * major + minor                                */
+
+/* ------------------------------------------------------------------ layouts */
+/* Bytes of a packed GEMM operand (A) holding M x K values: Mp * K * (2 | 1). */
+size_t frt_operand_bytes(int dtype, int M, int K);
+/* Bytes of a packed weight holding K x N values: K * N * (2 | 1). */
+size_t frt_weight_bytes(int dtype, int K, int N);
+
+/* Host-only layout helpers (no HIP call; used to inspect and build test data).
+ * Codes are bf16 bit patterns (uint16) or e4m3 codes (uint8), row-major logical order.
+ * pack writes every byte of `packed_host` (padding rows as zero codes).              */
+int frt_operand_pack_host(const void* codes_host, int dtype, int M, int K, void* packed_host);
+int frt_operand_unpack_host(const void* packed_host, int dtype, int M, int K, void* codes_host);
+int frt_weight_pack_host(const void* codes_host, int dtype, int K, int N, int layout,
+                         void* packed_host);
+int frt_weight_unpack_host(const void* packed_host, int dtype, int K, int N, int layout,
+                           void* codes_host);
+
+/* ------------------------------------------------------------------ offline weight prep */
+/* Pack a bf16 weight W [K][N] (row-major bits, device) for the skinny GEMM.
+ * gamma_dev [K] fp32 or NULL: fold a fixed RMSNorm gain into the weight,
+ *   W' = diag(gamma) W (notes, section "CUDA Graph 与图化简分别省掉什么", W' equation),
+ *   computed in fp32 and rounded once to the target format.
+ * dtype FRT_BF16: packed bf16 of W'.  colscale_dev ignored (may be NULL).
+ * dtype FRT_E4M3: per-output-channel scale s_w[n] = max_k |W'[k][n]| / 448 written to
+ *   colscale_dev [N] (fp32); codes e4m3(W'[k][n] / s_w[n]); a zero column gets s_w = 0
+ *   and zero codes (the notes' static-quantisation section keeps weight scales apart
+ *   from activation scales).
+ * layout: FRT_W_PLAIN or FRT_W_GATE_UP (N % 32 == 0).  w_packed_dev must hold
+ * frt_weight_bytes(dtype, K, N) bytes and must not overlap w_bf16_dev.              */
+int frt_pack_weight(void* stream, int K, int N, const uint16_t* w_bf16_dev,
+                    const float* gamma_dev, int dtype, int layout, void* w_packed_dev,
+                    float* colscale_dev);
+
+/* ------------------------------------------------------------------ producer */
+/* Gated residual + (Ada)RMSNorm + static-scale quantisation, one fused kernel.
+ *
+ *   x[m][k]  = (sum_{j=0..x_splits-1} x_dev[j][m][k]) * x_scale * x_colscale[k]
+ *              (partials summed in ascending j; x_colscale NULL = 1; x_dev NULL = no x)
+ *   h        = residual + gate[k] * x          (gate NULL = 1)
+ *   xhat     = h / sqrt(mean_k(h^2) + eps)     (notes, RMSNorm equation)
+ *   y        = xhat * (1 + ada_scale[k]) + ada_shift[k]   (NULL = 0; AdaRMSNorm)
+ *   operand  = bf16(y)  or  e4m3(y / act_scale)           (packed, Mp x K)
+ *
+ * x_dev [x_splits][M][K] fp32, residual_dev [M][K] fp32, residual_out_dev [M][K] fp32
+ * (NULL = h not stored; may equal residual_dev for an in-place update); vectors [K]
+ * fp32.  operand_out_dev: frt_operand_bytes(out_dtype, M, K) bytes, or NULL to only
+ * update the residual stream.  act_scale > 0 (used for FRT_E4M3 only).
+ * 1 <= x_splits <= 16; K % 32 (bf16) or % 128 (e4m3); K <= 4096; eps >= 0.           */
+int frt_residual_norm_quant(void* stream, int M, int K,
+                            const float* x_dev, int x_splits, float x_scale,
+                            const float* x_colscale_dev,
+                            const float* residual_dev, float* residual_out_dev,
+                            const float* gate_dev, const float* ada_scale_dev,
+                            const float* ada_shift_dev, float eps,
+                            int out_dtype, float act_scale, void* operand_out_dev);
+
+/* ------------------------------------------------------------------ skinny GEMM */
+/* C = A W with A the packed operand [Mp][K] and W the packed weight [K][N], both
+ * FRT_BF16 or both FRT_E4M3, MFMA with fp32 accumulation.  K is cut into `splits`
+ * contiguous equal chunks; chunk j's product is partial P_j (notes, split-K equation).
+ *
+ * splits: 1, 2, 4, 8 or 16, or 0 to let the library choose for (M, N, K, dtype).
+ * partials_dev [splits][M][N] fp32 workspace, partials_bytes >= splits*M*N*4; it may be
+ *   NULL (bytes 0) only when splits resolves to 1 and epi != FRT_EPI_NONE.
+ * Scale recovery: C = (sum_j P_j) * act_scale * w_colscale[n] (w_colscale NULL = 1).
+ * epi FRT_EPI_NONE: the partials are the result (a consumer reduces them later).
+ * epi STORE_F32 / STORE_BF16: out_dev [M][N].
+ * epi SILU_GATE_QUANT: needs layout FRT_W_GATE_UP; z = SiLU(C[:, :N/2]) * C[:, N/2:],
+ *   out_dev = packed operand of z (out_dtype FRT_BF16 or FRT_E4M3 with out_act_scale),
+ *   frt_operand_bytes(out_dtype, M, N/2) bytes.
+ * With splits == 1 the epilogue runs inside the GEMM kernel; otherwise a second
+ * (consumer) kernel reduces the partials in ascending j.                             */
+int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int splits,
+                           int ab_dtype, int layout, const void* a_packed_dev,
+                           const void* w_packed_dev, const float* w_colscale_dev,
+                           float act_scale, float* partials_dev, size_t partials_bytes,
+                           int epi, void* out_dev, int out_dtype, float out_act_scale);
+
+/* Split-K consumer on its own: reduce [splits][M][N] partials (ascending j), recover
+ * scales, then apply `epi` (STORE_F32, STORE_BF16 or SILU_GATE_QUANT; for the latter
+ * the columns are in logical order, gate = [0, N/2)).                                */
+int frt_splitk_reduce(void* stream, int M, int N, int splits, const float* partials_dev,
+                      float act_scale, const float* w_colscale_dev, int epi, void* out_dev,
+                      int out_dtype, float out_act_scale);
+
+/* Library's split-K choice for a GEMM shape (what splits = 0 resolves to). */
+int frt_splitk_choose(int M, int N, int K, int ab_dtype);
+
+/* ------------------------------------------------------------------ attention */
+/* Attention of the M action rows over a cached prefix (one KV head shared by n_heads
+ * query heads, no mask, scale 1/sqrt(head_dim)), fed straight from the fused QKV
+ * GEMM's partials.  Not on the pages; it is the step between the QKV and O GEMMs of
+ * the action-decoder layer.
+ *   qkv = (sum_j qkv_partials[j]) * qkv_act_scale * qkv_colscale[n], columns
+ *         [Q (n_heads*head_dim) | K (head_dim) | V (head_dim)], rounded to bf16;
+ *   keys / values = [prefix (prefix_len rows, bf16) ; own K / V (M rows)];
+ *   O[m][h*d + e] = softmax_t(q_h . k_t / sqrt(d)) v_t[e], fp32-accurate;
+ *   operand_out = packed bf16(O) or e4m3(O / out_act_scale), Mp x n_heads*head_dim.
+ * qkv_out_dev: NULL, or [M][(n_heads+2)*head_dim] bf16 bits receiving the rounded Q/K/V.
+ * head_dim == 128, 1 <= n_heads <= 16, 0 <= prefix_len <= 8192.                       */
+int frt_attention_prefix(void* stream, int M, int n_heads, int head_dim, int prefix_len,
+                         const float* qkv_partials_dev, int qkv_splits, float qkv_act_scale,
+                         const float* qkv_colscale_dev, const uint16_t* k_prefix_dev,
+                         const uint16_t* v_prefix_dev, int out_dtype, float out_act_scale,
+                         void* operand_out_dev, uint16_t* qkv_out_dev);
+
+/* ------------------------------------------------------------------ layer chain */
+/* One action-decoder layer (per layer l, per flow step k):
+ *   h   = h + gate_mlp(prev) * x_mlp(prev)             (previous layer's MLP output)
+ *   a   = quant(AdaRMSNorm(h; mod[k][l][0]))           producer
+ *   qkv = a W_qkv[l]                                   GEMM (split-K)
+ *   o   = quant(attention(qkv, prefix_k[l], prefix_v[l]))
+ *   x   = o W_o[l];  h = h + mod[k][l][0].gate * x     GEMM, then producer
+ *   b   = quant(AdaRMSNorm(h; mod[k][l][1]))
+ *   z   = quant(SiLU(b W_gate) * (b W_up))             GEMM + fused consumer
+ *   x_mlp = z W_down[l]                                GEMM; reduced by the next producer
+ * Flow steps compose: the residual stream leaving step k enters step k+1; after the
+ * last layer of the last step a final producer adds the last MLP output into "x".
+ * mod rows are (scale, shift, gate); the producer that starts layer l uses layer l's
+ * modulation while reducing layer l-1's output (next-layer conditioning prepares the
+ * next input: notes, static-quantisation section).                                   */
+typedef struct frt_chain_desc {
+  int layers, steps, M, hidden, n_heads, head_dim, prefix_len, mlp;
+  int dtype;                 /* FRT_BF16 or FRT_E4M3 (weights and GEMM inputs)          */
+  float eps;
+  int splits_qkv, splits_o, splits_up, splits_down;   /* 0 = library choice            */
+  int use_graph;             /* 1: capture once, replay with one hipGraphLaunch          */
+  int keep_intermediates;    /* 1: every (step, layer) writes its own debug buffers      */
+  /* host arrays of `layers` device pointers to packed weights (frt_pack_weight):
+   * qkv [hidden][(n_heads+2)*head_dim] plain, o [n_heads*head_dim][hidden] plain,
+   * up [hidden][2*mlp] FRT_W_GATE_UP, down [mlp][hidden] plain.                        */
+  const void* const* w_qkv;
+  const void* const* w_o;
+  const void* const* w_up;
+  const void* const* w_down;
+  /* e4m3 only: host arrays of `layers` device pointers to fp32 column scales. */
+  const float* const* s_qkv;
+  const float* const* s_o;
+  const float* const* s_up;
+  const float* const* s_down;
+} frt_chain_desc;
+
+typedef struct frt_chain frt_chain;
+
+/* Bytes of device memory the chain needs in the caller's arena (named buffers,
+ * operands, partials; plus debug buffers when keep_intermediates).  0 on bad desc.   */
+size_t frt_layer_chain_arena_bytes(const frt_chain_desc* desc);
+/* Bind the named buffers inside `arena_dev` (16-byte aligned, >= arena_bytes) and,
+ * with use_graph, capture the whole chain on `capture_stream` (synchronous). */
+int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_dev, size_t arena_bytes,
+                           void* capture_stream, frt_chain** out);
+/* Device address and size of a named buffer:
+ *   "x_in"      [M][hidden] fp32   residual stream entering the first layer of the first step
+ *   "x_out"     [M][hidden] fp32   residual stream after the last layer of the last step
+ *   "mod"       [steps][layers][2][3][hidden] fp32   (scale, shift, gate) per sublayer
+ *   "act_scale" [layers][4] fp32   static activation scales (e4m3): qkv, o, up, down inputs
+ *   "prefix_k", "prefix_v"  [layers][prefix_len][head_dim] bf16
+ *   "h"         [M][hidden] fp32   working residual stream (not kept per layer)
+ *   debug (keep_intermediates): "dbg_h_attn", "dbg_h_mlp" [steps][layers][M][hidden] fp32,
+ *   "dbg_a_qkv", "dbg_a_o", "dbg_a_up", "dbg_a_down" [steps][layers] packed operands,
+ *   "dbg_p_qkv", "dbg_p_o", "dbg_p_down" [steps][layers][splits][M][N] fp32 and
+ *   "dbg_qkv" [steps][layers][M][(n_heads+2)*head_dim] bf16; each (step, layer) slice
+ *   starts on a 256-byte boundary.  A name whose buffer is empty returns FRT_E_STATE. */
+int frt_layer_chain_buffer(frt_chain* chain, const char* name, void** dev, size_t* bytes);
+/* Run every step and layer once on `stream` (one hipGraphLaunch, or eager launches). */
+int frt_layer_chain_run(frt_chain* chain, void* stream);
+/* Kernels one run launches (graph nodes when captured). */
+int frt_layer_chain_kernel_count(const frt_chain* chain);
+int frt_layer_chain_destroy(frt_chain* chain);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FRT_H */

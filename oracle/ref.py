@@ -121,7 +121,11 @@ def residual_norm_quant(residual, x_parts=None, x_colscale=None, x_scale=1.0, ga
     h = gated_residual(residual, gate, x)
     xhat = rms_normalise(h, eps)
     y = ada_modulate(xhat, ada_scale, ada_shift)
-    mag = np.abs(ada_modulate(xhat, ada_scale, None))
+    # size of the summands of y: (|r| + |gate * x|) / rms scaled by |1 + scale|, plus |shift|
+    hmag = np.abs(gated_residual(np.abs(_f64(residual)), None if gate is None else np.abs(_f64(gate)),
+                                 None if x is None else np.abs(x)))
+    inv_rms = 1.0 / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+    mag = np.abs(ada_modulate(hmag * inv_rms, ada_scale, None))
     if ada_shift is not None:
         mag = mag + np.abs(_f64(ada_shift))[None, :]
     v, codes, deq = quantise(y, out_dtype, act_scale)
@@ -262,7 +266,7 @@ def _gemm_deq(a_deq, w_deq, act_scale, colscale):
 
 
 def layer(h, x_prev, gate_prev, mod_attn, mod_mlp, w, scales, k_prefix, v_prefix,
-          dims, dtype, eps, record=None, quantise_acts=True):
+          dims, dtype, eps, record=None, quantise_acts=True, trace=None, perturb=None):
     """One action-decoder layer.
 
     h: residual stream entering the layer before the previous sublayer's output is added;
@@ -272,11 +276,16 @@ def layer(h, x_prev, gate_prev, mod_attn, mod_mlp, w, scales, k_prefix, v_prefix
     scales: the 4 static activation scales of this layer (ignored for bf16).
     Returns (h_after_attn, x_mlp, gate_mlp): the next layer adds gate_mlp * x_mlp.
     With quantise_acts=False the GEMM inputs are not rounded (calibration run) and
-    record, when given, collects max|y| per site.
+    record, when given, collects max|y| per site.  trace, when given, receives the
+    intermediate values (residual streams, GEMM inputs as decoded codes, GEMM outputs).
+    perturb, when given, is applied to every GEMM input before it is rounded; it exists
+    only to measure how the chain itself amplifies tiny differences (sensitivity runs).
     """
     nh, hd = dims["n_heads"], dims["head_dim"]
 
     def q(v_val, site):
+        if perturb is not None:
+            v_val = perturb(v_val)
         if record is not None:
             record[site] = max(record.get(site, 0.0), float(np.max(np.abs(v_val))))
         if not quantise_acts:
@@ -287,31 +296,37 @@ def layer(h, x_prev, gate_prev, mod_attn, mod_mlp, w, scales, k_prefix, v_prefix
     # sublayer 1: gated residual of the previous MLP + AdaRMSNorm + quantise
     h = gated_residual(h, gate_prev, x_prev)
     y = ada_modulate(rms_normalise(h, eps), mod_attn[MOD_SCALE], mod_attn[MOD_SHIFT])
-    a, s_a = q(y, SITE_QKV)
-    c_qkv = _gemm_deq(a, w["qkv"], s_a, w.get("sqkv"))
+    a_qkv, s_a = q(y, SITE_QKV)
+    c_qkv = _gemm_deq(a_qkv, w["qkv"], s_a, w.get("sqkv"))
     qb, kb, vb = qkv_split_bf16(c_qkv, nh, hd)
     o, _ = attention_prefix(qb, np.concatenate([_f64(k_prefix), kb]),
                             np.concatenate([_f64(v_prefix), vb]), nh, hd)
-    a, s_a = q(o, SITE_O)
-    x_attn = _gemm_deq(a, w["o"], s_a, w.get("so"))
+    a_o, s_a = q(o, SITE_O)
+    x_attn = _gemm_deq(a_o, w["o"], s_a, w.get("so"))
+    if trace is not None:
+        trace.update(h_attn=h, a_qkv=a_qkv, c_qkv=c_qkv, qkv=np.concatenate([qb, kb, vb], axis=1),
+                     o=o, a_o=a_o, x_attn=x_attn)
     # sublayer 2
     h = gated_residual(h, mod_attn[MOD_GATE], x_attn)
     y = ada_modulate(rms_normalise(h, eps), mod_mlp[MOD_SCALE], mod_mlp[MOD_SHIFT])
-    a, s_a = q(y, SITE_UP)
-    c_up = _gemm_deq(a, w["up"], s_a, w.get("sup"))
+    a_up, s_a = q(y, SITE_UP)
+    c_up = _gemm_deq(a_up, w["up"], s_a, w.get("sup"))
     z = silu_gate(c_up)
-    a, s_a = q(z, SITE_DOWN)
-    x_mlp = _gemm_deq(a, w["down"], s_a, w.get("sdown"))
+    a_down, s_a = q(z, SITE_DOWN)
+    x_mlp = _gemm_deq(a_down, w["down"], s_a, w.get("sdown"))
+    if trace is not None:
+        trace.update(h_mlp=h, a_up=a_up, c_up=c_up, z=z, a_down=a_down, x_mlp=x_mlp)
     return h, x_mlp, _f64(mod_mlp[MOD_GATE])
 
 
 def chain(x0, weights, scales, k_prefix, v_prefix, mod, dims, dtype, eps,
-          record=None, quantise_acts=True):
+          record=None, quantise_acts=True, trace=None, perturb=None):
     """steps x layers application of ``layer`` (reading R10), then the final gated residual.
 
     weights: list over layers of dicts as in ``layer``; scales: [L][4]; k_prefix,
     v_prefix: [L][P][hd]; mod: [S][L][2][3][H].  Returns the residual stream after the
-    last layer of the last step.
+    last layer of the last step.  trace, when given (a dict), maps (k, l) to each
+    layer's intermediates.
     """
     mod = _f64(mod)
     S, L = mod.shape[0], mod.shape[1]
@@ -322,7 +337,9 @@ def chain(x0, weights, scales, k_prefix, v_prefix, mod, dims, dtype, eps,
                                          mod[k, l, SUB_MLP], weights[l], scales[l],
                                          k_prefix[l], v_prefix[l], dims, dtype, eps,
                                          record=None if record is None else record.setdefault((k, l), {}),
-                                         quantise_acts=quantise_acts)
+                                         quantise_acts=quantise_acts,
+                                         trace=None if trace is None else trace.setdefault((k, l), {}),
+                                         perturb=perturb)
     return gated_residual(h, gate_prev, x_prev)
 
 

@@ -103,9 +103,9 @@ def chain_dims(layers=18, steps=10, M=50, hidden=1024, n_heads=8, head_dim=128,
                 head_dim=head_dim, prefix=prefix, mlp=mlp)
 
 
-def workload4(dims, seed=TEST_SEED):
-    """Full chain inputs: X0, per-layer bf16 weights, prefix K/V (bf16), modulation table."""
-    L, S, M, H = dims["layers"], dims["steps"], dims["M"], dims["hidden"]
+def chain_weights(dims, seed=TEST_SEED):
+    """Per-layer bf16 weights and bf16 prefix K/V of the chain workload."""
+    L, H = dims["layers"], dims["hidden"]
     nh, hd, P, F = dims["n_heads"], dims["head_dim"], dims["prefix"], dims["mlp"]
     nqkv = (nh + 2) * hd
     layers = []
@@ -118,12 +118,30 @@ def workload4(dims, seed=TEST_SEED):
             down=weight_bf16(seed, 4, t + 3, F, H),
             k_prefix=to_bf16_bits(normal(seed, 4, t + 4, (P, hd))),
             v_prefix=to_bf16_bits(normal(seed, 4, t + 5, (P, hd)))))
+    return layers
+
+
+def chain_inputs(dims, seed=TEST_SEED):
+    """Residual stream X0 [M][H] and the modulation table [S][L][2][3][H] of one decision.
+
+    Flow step k has its conditioning vector c_k ~ N(0,1)^H; each (layer, sublayer) has
+    its own W_ada ~ N(0, 1/H)^(H x 3H); the (scale, shift, gate) rows are c_k W_ada.
+    """
+    L, S, M, H = dims["layers"], dims["steps"], dims["M"], dims["hidden"]
+    c = [normal(seed, 4, 20000 + k, (H,)).astype(np.float64) for k in range(S)]
     mod = np.zeros((S, L, 2, 3, H), np.float32)
-    for k in range(S):
-        for l in range(L):
-            for sub in range(2):
-                mod[k, l, sub] = modulation(seed, 4, 10000 + (k * L + l) * 2 + sub, H)
-    return dict(x0=normal(seed, 4, 0, (M, H)), layers=layers, mod=mod, dims=dims)
+    for l in range(L):
+        for sub in range(2):
+            w = normal(seed, 4, 30000 + 2 * l + sub, (H, 3 * H), std=1.0 / np.sqrt(H)).astype(np.float64)
+            for k in range(S):
+                mod[k, l, sub] = (c[k] @ w).astype(np.float32).reshape(3, H)
+    return normal(seed, 4, 0, (M, H)), mod
+
+
+def workload4(dims, seed=TEST_SEED, input_seed=None):
+    """Full chain: X0, per-layer bf16 weights, prefix K/V (bf16), modulation table."""
+    x0, mod = chain_inputs(dims, seed if input_seed is None else input_seed)
+    return dict(x0=x0, layers=chain_weights(dims, seed), mod=mod, dims=dims)
 
 
 def workload5(M, seed=TEST_SEED, K=2048, N=16384):

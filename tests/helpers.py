@@ -1,0 +1,62 @@
+"""Comparison helpers for the parity tests (test-side arithmetic only).
+
+Tie band: the oracle rounds float64 values, the GPU rounds float32 values computed in
+another order, so a code may legitimately differ where the exact value sits within the
+GPU's float32 error of a rounding boundary.  A GPU code is accepted when it is a correct
+rounding of some value within TAU * mag of the oracle's exact pre-rounding value v, i.e.
+when it lies (in value order) between encode(v - TAU*mag) and encode(v + TAU*mag); mag is
+the size of the summands that produced v, so cancellation cannot shrink the band below
+float32's own error.  TAU = 2**-17 is 128 float32 ulps of the summands.  Rounding is
+monotone, so the interval test is exact.
+"""
+import numpy as np
+
+from oracle import codec
+
+TAU = 2.0 ** -17
+
+
+def _ordinal(codes, dtype):
+    c = np.asarray(codes).astype(np.int64)
+    if dtype == "bf16":
+        mag, sign = c & 0x7FFF, (c >> 15) & 1
+    else:
+        mag, sign = c & 0x7F, (c >> 7) & 1
+    return np.where(sign == 1, -mag, mag)
+
+
+def check_codes(gpu_codes, v, mag, dtype, tau=TAU, max_frac=0.01, label=""):
+    """Assert GPU codes equal the oracle's up to the tie band; return (n_diff, n_total)."""
+    gpu_codes = np.asarray(gpu_codes)
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.broadcast_to(np.asarray(mag, dtype=np.float64), v.shape)
+    want = codec.encode(v, dtype)
+    assert gpu_codes.shape == want.shape, (gpu_codes.shape, want.shape)
+    diff = np.flatnonzero(gpu_codes.ravel() != want.ravel())
+    if len(diff):
+        vv = v.ravel()[diff]
+        band = tau * mag.ravel()[diff]
+        lo = _ordinal(codec.encode(vv - band, dtype), dtype)
+        hi = _ordinal(codec.encode(vv + band, dtype), dtype)
+        g = _ordinal(gpu_codes.ravel()[diff], dtype)
+        ok = (g >= lo) & (g <= hi)
+        bad = diff[~ok]
+        if len(bad):
+            i = bad[0]
+            raise AssertionError(
+                f"{label}: {len(bad)} codes outside the tie band of {len(diff)} differing "
+                f"(of {v.size}); first at flat index {i}: gpu {int(gpu_codes.ravel()[i]):#x} "
+                f"oracle {int(want.ravel()[i]):#x} value {v.ravel()[i]!r} mag {mag.ravel()[i]!r}")
+    assert len(diff) <= max_frac * v.size, f"{label}: {len(diff)} of {v.size} codes differ"
+    return len(diff), v.size
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b.ravel())
+    return float(np.linalg.norm((a - b).ravel()) / (den if den > 0 else 1.0))
+
+
+def bf16_values(bits):
+    return codec.bf16_decode(np.asarray(bits).view(np.uint16))

@@ -1,0 +1,121 @@
+"""GPU parity of the whole action-decoder chain against the oracle chain (MI355X only).
+
+Both sides start from the same seeded inputs and bf16 master weights; each quantises the
+weights itself (the packing kernel's codes are checked in test_gpu_kernels.py).
+
+- The first GEMM input (layer 0, step 0) depends only on the chain's inputs, so its codes
+  must match the oracle's up to the tie band (a check of the chain's buffer, modulation
+  and scale wiring for that site).
+- End to end and at every layer-step's residual streams, the bar is derived from the
+  oracle chain's own sensitivity: the oracle is rerun with every GEMM input perturbed by
+  relative noise before rounding, and the GPU must stay within a multiple of the
+  divergence that causes.  bf16: noise 2^-22 (a few float32 ulps, the size of the GPU's
+  own arithmetic differences), bar 8x.  e4m3: a value next to a rounding boundary flips
+  to the neighbouring code (a 6% step) and later layers amplify the flip, and with so
+  few flips per run their count is itself random, so the noise is the tie band's own
+  width (2^-17, the largest per-quantisation difference the kernel tests accept) and
+  the bar is 2x.  Exact parity of each kernel is tested in test_gpu_kernels.py.
+- Graph replay must equal eager launches bit for bit, and two replays must agree bit for
+  bit (the pages' state-reuse result keeps outputs bit-identical; replay reuses the same
+  arguments and addresses).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import codec, ref
+from tests.helpers import check_codes, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X GPU")
+    from gemm_chains_amd import chain, frt
+    frt.lib()
+    return frt, chain
+
+
+def _oracle_weights(layers, dtype):
+    ws = []
+    for lw in layers:
+        d = {}
+        for name in ("qkv", "o", "up", "down"):
+            codes, s_w, _ = ref.pack_weight_values(codec.bf16_decode(lw[name]), None, dtype)
+            d[name] = codec.decode(codes, dtype)
+            if s_w is not None:
+                d["s" + name] = s_w
+        ws.append(d)
+    return ws
+
+
+def _oracle_run(wl, ws, scales, dtype, trace=None, perturb=None):
+    L = wl["dims"]["layers"]
+    kp = [codec.bf16_decode(l["k_prefix"]) for l in wl["layers"]]
+    vp = [codec.bf16_decode(l["v_prefix"]) for l in wl["layers"]]
+    return ref.chain(wl["x0"], ws, scales if scales is not None else np.ones((L, 4)),
+                     kp, vp, wl["mod"], wl["dims"], dtype, 1e-6, trace=trace, perturb=perturb)
+
+
+@pytest.mark.parametrize("dtype,M,splits", [("bf16", 50, (0, 0, 0, 0)), ("e4m3", 50, (0, 0, 0, 0)),
+                                            ("bf16", 10, (2, 1, 2, 8)), ("e4m3", 10, (1, 2, 1, 4))])
+def test_chain_parity(F, dtype, M, splits):
+    frt, chain = F
+    dims = synth.chain_dims(layers=2, steps=2, M=M)
+    wl = synth.workload4(dims)
+    dt = frt.DTYPES[dtype]
+    ws = _oracle_weights(wl["layers"], dtype)
+    scales = None
+    if dtype == "e4m3":
+        x0c, modc = synth.chain_inputs(dims, synth.CAL_SEED)
+        kp = [codec.bf16_decode(l["k_prefix"]) for l in wl["layers"]]
+        vp = [codec.bf16_decode(l["v_prefix"]) for l in wl["layers"]]
+        scales = ref.calibrate(x0c, ws, kp, vp, modc, dims, 1e-6)
+    trace = {}
+    want = _oracle_run(wl, ws, scales, dtype, trace=trace)
+    g = np.random.default_rng(95)
+    noise, mult = (2.0 ** -22, 8) if dtype == "bf16" else (2.0 ** -17, 2)
+    sens = rel_l2(_oracle_run(wl, ws, scales, dtype,
+                              perturb=lambda v: v * (1.0 + noise * g.standard_normal(v.shape))), want)
+    bar = mult * max(sens, 1e-6 / mult)
+
+    packed = chain.PackedLayers(wl["layers"], dims, dt)
+    cg = chain.Chain(dims, packed, splits=splits, use_graph=True, keep_intermediates=True)
+    chain.load_workload(cg, wl, scales)
+    cg.run()
+    torch.cuda.synchronize()
+    got = cg.read("x_out").reshape(M, -1)
+    err = rel_l2(got, want)
+    print(f"chain {dtype} M={M}: rel L2 {err:.3e}, oracle sensitivity {sens:.3e}, bar {bar:.3e}, "
+          f"kernels {cg.kernel_count()}")
+    assert err <= bar
+    # the first GEMM input depends on the chain inputs only: codes exact up to the tie band
+    first = ref.residual_norm_quant(wl["x0"], ada_scale=wl["mod"][0, 0, 0, 0], ada_shift=wl["mod"][0, 0, 0, 1],
+                                    eps=1e-6, out_dtype=dtype, act_scale=1.0 if scales is None else scales[0][0])
+    Mp = 16 * ((M + 15) // 16)
+    opb = frt.frt_operand_bytes(dt, M, dims["hidden"])
+    a0 = cg.read("dbg_a_qkv")[:opb]
+    check_codes(frt.frt_operand_unpack_host(a0, dt, Mp, dims["hidden"])[:M], first["v"], first["mag"], dtype,
+                label="first GEMM input of the chain")
+    # every layer-step's residual streams
+    S, L, H = dims["steps"], dims["layers"], dims["hidden"]
+    h_attn = cg.read("dbg_h_attn").reshape(S, L, M, H)
+    h_mlp = cg.read("dbg_h_mlp").reshape(S, L, M, H)
+    for k in range(S):
+        for l in range(L):
+            assert rel_l2(h_attn[k, l], trace[(k, l)]["h_attn"]) <= bar, (k, l, "h_attn")
+            assert rel_l2(h_mlp[k, l], trace[(k, l)]["h_mlp"]) <= bar, (k, l, "h_mlp")
+    # replay twice: bit-identical; eager launches of the same chain: bit-identical
+    cg.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(cg.read("x_out").reshape(M, -1), got)
+    ce = chain.Chain(dims, packed, splits=splits, use_graph=False, keep_intermediates=False)
+    chain.load_workload(ce, wl, scales)
+    ce.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(ce.read("x_out").reshape(M, -1), got), "eager vs graph replay"
+    cg.close()
+    ce.close()

@@ -1,0 +1,302 @@
+"""GPU parity of each kernel against the oracle, through the C ABI (MI355X only).
+
+Inputs are seeded and synthetic; both sides receive the same inputs (the oracle never
+takes a GPU output as input).  Where an upstream float32 step feeds a rounding inside a
+kernel, the inputs are chosen so that step is exact in float32 (dyadic values, power-of-
+two scales), so the two sides round the same value.
+
+Bars: codes bit-exact up to the tie band (tests/helpers.py); fp32 partial sums within
+relative L2 1e-5 of the float64 products for bf16 (fp32 accumulation of exact products)
+and 1e-4 for e4m3 (the 16x16x128 fp8 MFMA sums its 128 exact products with less than
+fp32 precision inside the instruction: ~1.5e-5 measured); bf16 GEMM outputs within
+relative L2 5e-3 and fp8 outputs within 2e-3 of the emulating oracle; split-K against
+unsplit within 1e-5 (bf16) and 1e-4 (e4m3).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import codec, ref
+from tests.helpers import check_codes, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X GPU")
+    from gemm_chains_amd import frt, device
+    frt.lib()  # raises if the HIP library is missing
+    return frt, device
+
+
+def _i16(a):
+    return np.ascontiguousarray(a).view(np.int16)
+
+
+def _u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ producer
+
+PRODUCER_CASES = [
+    # M, K, dtype, x_splits, gate, ada, colscale
+    (10, 1024, "bf16", 0, False, False, False),      # plain RMSNorm of the residual (gamma folded)
+    (10, 1024, "bf16", 4, True, True, False),
+    (50, 1024, "bf16", 1, True, True, False),
+    (50, 1024, "e4m3", 2, True, True, True),
+    (10, 1024, "e4m3", 4, True, True, True),
+    (64, 2048, "bf16", 8, True, False, False),
+    (1, 128, "e4m3", 16, False, True, True),
+    (17, 4096, "bf16", 3, True, True, False),
+]
+
+
+@pytest.mark.parametrize("M,K,dtype,splits,use_gate,use_ada,use_cs", PRODUCER_CASES)
+def test_producer_parity(F, M, K, dtype, splits, use_gate, use_ada, use_cs):
+    frt, dev = F
+    dt = frt.DTYPES[dtype]
+    seed = 1000 + M * 7 + K + splits
+    r = synth.normal(seed, 90, 0, (M, K))
+    parts = synth.normal(seed, 90, 1, (max(splits, 1), M, K)) if splits else None
+    gate = synth.normal(seed, 90, 2, (K,)) if use_gate else None
+    sc = synth.normal(seed, 90, 3, (K,), std=0.5) if use_ada else None
+    sh = synth.normal(seed, 90, 4, (K,), std=0.5) if use_ada else None
+    cs = np.abs(synth.normal(seed, 90, 5, (K,), std=0.01)) + np.float32(1e-3) if use_cs else None
+    x_scale = np.float32(0.75)
+    eps = 1e-6
+    o0 = ref.residual_norm_quant(r, parts, cs, float(x_scale), gate, sc, sh, eps, dtype, 1.0)
+    # a static scale that saturates the largest ~1% of values (tests the clamp)
+    act = float(np.float32(np.quantile(np.abs(o0["y"]), 0.99) / 448.0)) if dtype == "e4m3" else 1.0
+    o = ref.residual_norm_quant(r, parts, cs, float(x_scale), gate, sc, sh, eps, dtype, act)
+
+    T = dev.to_dev
+    h_out = dev.empty_f32(M, K)
+    op = dev.empty_bytes(frt.frt_operand_bytes(dt, M, K))
+    op.fill_(0xAB)
+    frt.frt_residual_norm_quant(M, K, T(parts) if splits else None, splits if splits else 1, float(x_scale),
+                                T(cs) if use_cs else None, T(r), h_out, T(gate) if use_gate else None,
+                                T(sc) if use_ada else None, T(sh) if use_ada else None, eps, dt, act, op)
+    torch.cuda.synchronize()
+    h = dev.to_np(h_out)
+    # float32 error bound of h = r + gate * (sum_j P_j) * x_scale * colscale: a few ulps of
+    # the summands' magnitudes
+    hmag = np.abs(r).astype(np.float64)
+    if splits:
+        xs_mag = np.sum(np.abs(parts.astype(np.float64)), axis=0) * float(x_scale)
+        if use_cs:
+            xs_mag = xs_mag * cs[None, :]
+        if use_gate:
+            xs_mag = xs_mag * np.abs(gate)[None, :]
+        hmag = hmag + xs_mag
+    assert np.all(np.abs(h - o["h"]) <= 2.0 ** -20 * hmag), "residual stream"
+    Mp = 16 * math.ceil(M / 16)
+    codes = dev.operand_codes(op, dt, Mp, K)
+    check_codes(codes[:M], o["v"], o["mag"], dtype, label=f"producer {dtype} M={M}")
+    assert np.all(codes[M:] == 0), "padding rows must hold zero codes"
+
+
+def test_producer_inplace_and_residual_only(F):
+    frt, dev = F
+    M, K = 50, 1024
+    r = synth.normal(5, 91, 0, (M, K))
+    x = synth.normal(5, 91, 1, (2, M, K))
+    g = synth.normal(5, 91, 2, (K,))
+    o = ref.residual_norm_quant(r, x, None, 1.0, g, None, None, 1e-6, "bf16", 1.0)
+    buf = dev.to_dev(r)
+    frt.frt_residual_norm_quant(M, K, dev.to_dev(x), 2, 1.0, None, buf, buf, dev.to_dev(g), None, None, 1e-6,
+                                frt.BF16, 1.0, None)
+    torch.cuda.synchronize()
+    assert np.allclose(dev.to_np(buf), o["h"], rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------------------------ weight packing
+
+@pytest.mark.parametrize("K,N,dtype,layout,gamma", [
+    (1024, 1024, "bf16", 0, True), (1024, 1024, "bf16", 0, False), (1024, 8192, "bf16", 1, False),
+    (1024, 2560, "e4m3", 0, False), (4096, 1024, "e4m3", 0, False), (1024, 8192, "e4m3", 1, True),
+    (128, 48, "e4m3", 0, False), (32, 16, "bf16", 0, True)])
+def test_pack_weight_parity(F, K, N, dtype, layout, gamma):
+    frt, dev = F
+    dt = frt.DTYPES[dtype]
+    w = synth.weight_bf16(77, 92, K + N, K, N)
+    if dtype == "e4m3" and N >= 48:
+        w[:, 7] = 0                                  # an all-zero column: s_w = 0, zero codes
+    g = synth.normal(77, 92, 1, (K,), std=0.1, mean=1.0) if gamma else None
+    packed, cs = dev.pack_weight(w, dt, layout, gamma=g)
+    torch.cuda.synchronize()
+    codes = dev.weight_codes(packed, dt, K, N, layout)
+    ocodes, s_w, v = ref.pack_weight_values(codec.bf16_decode(w), g, dtype)
+    if dtype == "bf16":
+        mag = np.abs(v)
+        check_codes(codes, v, mag, "bf16", label="packed bf16 weight")
+        if not gamma:
+            assert np.array_equal(codes, w), "bf16 weights without gamma pack bit-exactly"
+    else:
+        gs = dev.to_np(cs).astype(np.float64)
+        if gamma:
+            assert np.allclose(gs, s_w, rtol=2.0 ** -22, atol=0)
+        else:
+            assert np.array_equal(gs, s_w), "column scales are exact without gamma"
+        check_codes(codes, v, np.abs(v), "e4m3", label="packed e4m3 weight")
+        if N >= 48:
+            assert np.all(codes[:, 7] == 0) and gs[7] == 0.0
+
+
+# ------------------------------------------------------------------ GEMM
+
+def _gemm_inputs(frt, dev, M, N, K, dtype, seed, layout=0):
+    """Oracle-prepared codes for A and W, host-packed into the GPU layout."""
+    dt = frt.DTYPES[dtype]
+    w_bits = synth.weight_bf16(seed, 93, 1, K, N)
+    wcodes, s_w, _ = ref.pack_weight_values(codec.bf16_decode(w_bits), None, dtype)
+    a_val = synth.normal(seed, 93, 2, (M, K))
+    if dtype == "bf16":
+        acodes = synth.to_bf16_bits(a_val)
+    else:
+        acodes = codec.e4m3_encode(a_val.astype(np.float64) * 60.0)
+    a_pk = dev.to_dev(frt.frt_operand_pack_host(acodes, dt, M, K))
+    w_pk = dev.to_dev(frt.frt_weight_pack_host(wcodes, dt, K, N, layout))
+    a_dec = codec.decode(acodes, dtype)
+    w_dec = codec.decode(wcodes, dtype)
+    return dt, a_pk, w_pk, a_dec, w_dec, s_w
+
+
+GEMM_CASES = [
+    # M, N, K, dtype, splits
+    (10, 1024, 1024, "bf16", 1), (10, 1024, 1024, "bf16", 2), (10, 1024, 1024, "bf16", 4),
+    (50, 8192, 1024, "bf16", 1), (50, 8192, 1024, "bf16", 4), (50, 8192, 1024, "bf16", 8),
+    (50, 1024, 4096, "bf16", 1), (50, 1024, 4096, "bf16", 4), (50, 1024, 4096, "bf16", 8),
+    (10, 2560, 1024, "e4m3", 1), (10, 8192, 1024, "e4m3", 2), (10, 1024, 4096, "e4m3", 4),
+    (50, 1280, 1024, "e4m3", 4), (64, 16384, 2048, "bf16", 2), (1, 16384, 2048, "e4m3", 4),
+    (1, 16, 32, "bf16", 1), (17, 48, 96, "bf16", 1), (33, 32, 128, "e4m3", 1),
+    (64, 64, 512, "bf16", 16), (49, 1024, 1024, "e4m3", 8),
+]
+
+
+@pytest.mark.parametrize("M,N,K,dtype,splits", GEMM_CASES)
+def test_gemm_partials_parity(F, M, N, K, dtype, splits):
+    frt, dev = F
+    dt, a_pk, w_pk, a_dec, w_dec, s_w = _gemm_inputs(frt, dev, M, N, K, dtype, seed=M * 31 + N + K)
+    parts = dev.empty_f32(splits, M, N)
+    frt.frt_skinny_gemm_splitk(M, N, K, splits, dt, frt.W_PLAIN, a_pk, w_pk, None, 1.0, parts,
+                               parts.numel() * 4, frt.EPI_NONE, None, dt, 1.0)
+    torch.cuda.synchronize()
+    got = dev.to_np(parts)
+    want = ref.gemm_splitk(a_dec, w_dec, splits)
+    acc_bar = 1e-5 if dtype == "bf16" else 1e-4
+    for j in range(splits):
+        assert rel_l2(got[j], want[j]) <= acc_bar, f"partial {j}"
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(10, 1024, 1024, "bf16"), (50, 1024, 4096, "e4m3"),
+                                         (64, 16384, 2048, "e4m3"), (16, 2560, 1024, "bf16")])
+def test_gemm_store_epilogues_and_splitk_invariance(F, M, N, K, dtype):
+    frt, dev = F
+    dt, a_pk, w_pk, a_dec, w_dec, s_w = _gemm_inputs(frt, dev, M, N, K, dtype, seed=7 + M + N)
+    act = 0.03125 if dtype == "e4m3" else 1.0
+    cs = dev.to_dev(s_w.astype(np.float32)) if dtype == "e4m3" else None
+    c_o = ref.reduce_partials(ref.gemm_splitk(a_dec, w_dec, 1), act, s_w)
+    g_mag = (np.abs(a_dec) @ np.abs(w_dec)) * act * (s_w[None, :] if s_w is not None else 1.0)
+    outs = {}
+    for s in (1, 2, 4):
+        if (K // (32 if dtype == "bf16" else 128)) % s:
+            continue
+        parts = dev.empty_f32(s, M, N)
+        c32 = dev.empty_f32(M, N)
+        frt.frt_skinny_gemm_splitk(M, N, K, s, dt, frt.W_PLAIN, a_pk, w_pk, cs, act, parts, parts.numel() * 4,
+                                   frt.EPI_STORE_F32, c32, frt.F32, 1.0)
+        cb = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        frt.frt_skinny_gemm_splitk(M, N, K, s, dt, frt.W_PLAIN, a_pk, w_pk, cs, act, parts, parts.numel() * 4,
+                                   frt.EPI_STORE_BF16, cb, frt.BF16, 1.0)
+        torch.cuda.synchronize()
+        outs[s] = dev.to_np(c32)
+        tol = 5e-3 if dtype == "bf16" else 2e-3
+        acc_bar = 1e-5 if dtype == "bf16" else 1e-4
+        assert rel_l2(outs[s], c_o) <= min(tol, acc_bar)
+        bits = _u16(cb)
+        assert rel_l2(codec.bf16_decode(bits), c_o) <= 5e-3
+        # an fp8 GEMM's outputs carry the MFMA's ~2^-16 internal rounding, so ~1% of their
+        # bf16 roundings sit within that error of a midpoint (all inside the tie band)
+        check_codes(bits, c_o, g_mag, "bf16", max_frac=0.01 if dtype == "bf16" else 0.05,
+                    label=f"bf16 store s={s}")
+    for s in outs:
+        assert rel_l2(outs[s], outs[1]) <= (1e-5 if dtype == "bf16" else 1e-4), f"split {s} vs unsplit"
+        print(f"split {s} vs unsplit rel L2 {rel_l2(outs[s], outs[1]):.2e}")
+
+
+@pytest.mark.parametrize("M,N,K,dtype,splits", [(50, 8192, 1024, "bf16", 1), (50, 8192, 1024, "bf16", 4),
+                                                (10, 8192, 1024, "e4m3", 1), (10, 8192, 1024, "e4m3", 2),
+                                                (64, 256, 256, "bf16", 1), (3, 512, 128, "e4m3", 1)])
+def test_gemm_silu_gate_epilogue(F, M, N, K, dtype, splits):
+    frt, dev = F
+    layout = frt.W_GATE_UP
+    dt, a_pk, w_pk, a_dec, w_dec, s_w = _gemm_inputs(frt, dev, M, N, K, dtype, seed=11 + M + N, layout=layout)
+    act = 0.015625 if dtype == "e4m3" else 1.0
+    cs = dev.to_dev(s_w.astype(np.float32)) if dtype == "e4m3" else None
+    c_o = ref.reduce_partials(ref.gemm_splitk(a_dec, w_dec, 1), act, s_w)
+    g_mag = (np.abs(a_dec) @ np.abs(w_dec)) * act * (s_w[None, :] if s_w is not None else 1.0)
+    n2 = N // 2
+    out_scale = float(np.float32(np.quantile(np.abs(ref.silu_gate(c_o)), 0.995) / 448.0)) if dtype == "e4m3" else 1.0
+    o = ref.silu_gate_quant(c_o, dtype, out_scale)
+    gte, up = c_o[:, :n2], c_o[:, n2:]
+    # summand sizes: the GEMM sums feeding gate and up (|SiLU'| <= 1.1) and the product itself
+    mag = 1.1 * np.abs(up) * g_mag[:, :n2] + np.abs(ref.silu(gte)) * g_mag[:, n2:] + np.abs(ref.silu(gte) * up)
+    if dtype == "e4m3":
+        mag = mag / out_scale
+    out = dev.empty_bytes(frt.frt_operand_bytes(dt, M, n2))
+    out.fill_(0xCD)
+    parts = dev.empty_f32(splits, M, N) if splits > 1 else None
+    frt.frt_skinny_gemm_splitk(M, N, K, splits, dt, layout, a_pk, w_pk, cs, act, parts,
+                               0 if parts is None else parts.numel() * 4, frt.EPI_SILU_GATE_QUANT, out, dt, out_scale)
+    torch.cuda.synchronize()
+    Mp = 16 * math.ceil(M / 16)
+    codes = dev.operand_codes(out, dt, Mp, n2)
+    check_codes(codes[:M], o["v"], mag, dtype, label=f"silu gate {dtype} s={splits}")
+    assert np.all(codes[M:] == 0)
+
+
+# ------------------------------------------------------------------ attention
+
+def _dyadic(seed, shape, scale_bits=10):
+    """Values k * 2^-scale_bits with |k| < 2^12: float32 sums of up to 16 stay exact."""
+    g = np.random.default_rng(seed)
+    return (g.integers(-2 ** 11, 2 ** 11, size=shape) * 2.0 ** -scale_bits).astype(np.float32)
+
+
+@pytest.mark.parametrize("M,splits,out_dtype,prefix,colscale", [
+    (50, 4, "bf16", 800, False), (10, 1, "e4m3", 800, True), (50, 2, "e4m3", 800, True),
+    (1, 1, "bf16", 0, False), (64, 8, "bf16", 37, False), (17, 1, "bf16", 800, False)])
+def test_attention_parity(F, M, splits, out_dtype, prefix, colscale):
+    frt, dev = F
+    nh, hd = 8, 128
+    nqkv = (nh + 2) * hd
+    dt = frt.DTYPES[out_dtype]
+    parts = _dyadic(M + splits, (splits, M, nqkv)) / np.float32(splits)
+    act = 0.5 if colscale else 1.0
+    cs = (2.0 ** np.random.default_rng(3).integers(-2, 2, nqkv)).astype(np.float32) if colscale else None
+    kp = synth.to_bf16_bits(synth.normal(3, 94, 0, (prefix, hd))) if prefix else np.zeros((0, hd), np.uint16)
+    vp = synth.to_bf16_bits(synth.normal(3, 94, 1, (prefix, hd))) if prefix else np.zeros((0, hd), np.uint16)
+    c = ref.reduce_partials(parts, act, cs)
+    o_full = ref.attention_block(c, codec.bf16_decode(kp), codec.bf16_decode(vp), nh, hd, out_dtype, 1.0)
+    out_scale = float(np.float32(np.max(np.abs(o_full["o"])) / 448.0)) if out_dtype == "e4m3" else 1.0
+    o = ref.attention_block(c, codec.bf16_decode(kp), codec.bf16_decode(vp), nh, hd, out_dtype, out_scale)
+    op = dev.empty_bytes(frt.frt_operand_bytes(dt, M, nh * hd))
+    qkv_out = torch.empty((M, nqkv), dtype=torch.int16, device="cuda")
+    kp_t = dev.to_dev(_i16(kp)) if prefix else None
+    vp_t = dev.to_dev(_i16(vp)) if prefix else None
+    frt.frt_attention_prefix(M, nh, hd, prefix, dev.to_dev(parts), splits, act, dev.to_dev(cs) if colscale else None,
+                             kp_t, vp_t, dt, out_scale, op, qkv_out)
+    torch.cuda.synchronize()
+    q_bits = _u16(qkv_out)
+    want_q = codec.bf16_encode(np.concatenate([o["q"], o["k"], o["v_own"]], axis=1))
+    assert np.array_equal(q_bits, want_q), "exact inputs: Q/K/V bf16 codes must match bit for bit"
+    Mp = 16 * math.ceil(M / 16)
+    codes = dev.operand_codes(op, dt, Mp, nh * hd)
+    check_codes(codes[:M], o["v"], o["mag"], out_dtype, label=f"attention {out_dtype} M={M}")
+    assert np.all(codes[M:] == 0)
