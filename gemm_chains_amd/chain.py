@@ -6,9 +6,9 @@ import torch
 from . import device, frt
 
 BUFFER_DTYPES = {"x_in": np.float32, "x_out": np.float32, "mod": np.float32, "act_scale": np.float32,
-                 "prefix_k": np.int16, "prefix_v": np.int16, "h": np.float32,
-                 "dbg_h_attn": np.float32, "dbg_h_mlp": np.float32, "dbg_p_qkv": np.float32,
-                 "dbg_p_o": np.float32, "dbg_p_down": np.float32, "dbg_qkv": np.int16,
+                 "k_cache": np.int16, "v_cache": np.int16, "h": np.float32,
+                 "dbg_h_attn": np.float32, "dbg_h_mlp": np.float32,
+                 "dbg_p_o": np.float32, "dbg_p_down": np.float32, "dbg_q": np.int16,
                  "dbg_a_qkv": np.uint8, "dbg_a_o": np.uint8, "dbg_a_up": np.uint8, "dbg_a_down": np.uint8}
 _TORCH = {np.float32: torch.float32, np.int16: torch.int16, np.uint8: torch.uint8}
 
@@ -92,8 +92,16 @@ def load_workload(chain, wl, act_scales=None):
     chain.write("mod", wl["mod"])
     d = wl["dims"]
     if d["prefix"]:
-        chain.write("prefix_k", np.stack([l["k_prefix"] for l in wl["layers"]]))
-        chain.write("prefix_v", np.stack([l["v_prefix"] for l in wl["layers"]]))
+        # prefix keys at the head of each layer's key cache; prefix values transposed at the
+        # head of each row of the value cache; the own rows are written by the chain
+        P, hd, T = d["prefix"], d["head_dim"], d["prefix"] + d["M"]
+        ldv = (T + 31) // 32 * 32
+        kc = chain.view("k_cache").view(d["layers"], T, hd)
+        vc = chain.view("v_cache").view(d["layers"], hd, ldv)
+        for l, lw in enumerate(wl["layers"]):
+            kc[l, :P].copy_(torch.from_numpy(np.ascontiguousarray(lw["k_prefix"]).view(np.int16)).to(device.DEV))
+            vt = np.ascontiguousarray(np.asarray(lw["v_prefix"]).T).view(np.int16)
+            vc[l, :, :P].copy_(torch.from_numpy(vt).to(device.DEV))
     L = d["layers"]
     chain.write("act_scale", np.ones((L, 4), np.float32) if act_scales is None
                 else np.asarray(act_scales, np.float32).reshape(L, 4))

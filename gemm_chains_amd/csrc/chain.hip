@@ -28,10 +28,13 @@ struct Buf {
 struct ChainLayout {
   int s_qkv = 0, s_o = 0, s_up = 0, s_down = 0;
   int nqkv = 0, nattn = 0;
+  int kv_len = 0;                                          // prefix + own rows
+  int ldv = 0;                                             // V^T row length (kv_len padded to 32)
   size_t op_qkv = 0, op_o = 0, op_up = 0, op_down = 0;     // operand bytes
   size_t pq = 0, po = 0, pu = 0, pd = 0;                   // partial bytes (one copy)
-  Buf x_in, x_out, mod, act, pk, pv, h, a_qkv, a_o, a_up, a_down, p_qkv, p_o, p_up, p_down;
-  Buf d_h_attn, d_h_mlp, d_a_qkv, d_a_o, d_a_up, d_a_down, d_p_qkv, d_p_o, d_p_down, d_qkv;
+  size_t qb = 0, attn_ws = 0;
+  Buf x_in, x_out, mod, act, kc, vc, h, q, aws, a_qkv, a_o, a_up, a_down, p_qkv, p_o, p_up, p_down;
+  Buf d_h_attn, d_h_mlp, d_a_qkv, d_a_o, d_a_up, d_a_down, d_p_o, d_p_down, d_q;
   size_t total = 0;
 };
 
@@ -68,18 +71,18 @@ static int validate_desc(const frt_chain_desc* d) {
   return FRT_OK;
 }
 
-static int resolve_split(int s, int M, int N, int K, int dtype) {
-  return s ? s : choose_splits(M, N, K, dtype);
+static int resolve_split(int s, int M, int N, int K, int dtype, int epi) {
+  return s ? s : choose_splits(M, N, K, dtype, epi);
 }
 
 static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
   const int M = d->M, H = d->hidden, F = d->mlp, dt = d->dtype;
   L.nqkv = (d->n_heads + 2) * d->head_dim;
   L.nattn = d->n_heads * d->head_dim;
-  L.s_qkv = resolve_split(d->splits_qkv, M, L.nqkv, H, dt);
-  L.s_o = resolve_split(d->splits_o, M, H, L.nattn, dt);
-  L.s_up = resolve_split(d->splits_up, M, 2 * F, H, dt);
-  L.s_down = resolve_split(d->splits_down, M, H, F, dt);
+  L.s_qkv = resolve_split(d->splits_qkv, M, L.nqkv, H, dt, kEpiQkv);
+  L.s_o = resolve_split(d->splits_o, M, H, L.nattn, dt, FRT_EPI_NONE);
+  L.s_up = resolve_split(d->splits_up, M, 2 * F, H, dt, FRT_EPI_SILU_GATE_QUANT);
+  L.s_down = resolve_split(d->splits_down, M, H, F, dt, FRT_EPI_NONE);
   const int ks = kstep_of(dt);
   FRT_CHECK((H / ks) % L.s_qkv == 0 && (L.nattn / ks) % L.s_o == 0 && (H / ks) % L.s_up == 0 &&
                 (F / ks) % L.s_down == 0,
@@ -88,7 +91,11 @@ static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
   L.op_o = frt_operand_bytes(dt, M, L.nattn);
   L.op_up = frt_operand_bytes(dt, M, H);
   L.op_down = frt_operand_bytes(dt, M, F);
-  L.pq = (size_t)L.s_qkv * M * L.nqkv * 4;
+  L.kv_len = d->prefix_len + M;
+  L.ldv = (L.kv_len + 31) / 32 * 32;
+  L.pq = L.s_qkv > 1 ? (size_t)L.s_qkv * M * L.nqkv * 4 : 0;
+  L.qb = (size_t)M * L.nattn * 2;
+  L.attn_ws = attention_workspace_bytes(M, d->n_heads, L.kv_len);
   L.po = (size_t)L.s_o * M * H * 4;
   L.pu = L.s_up > 1 ? (size_t)L.s_up * M * 2 * F * 4 : 0;
   L.pd = (size_t)L.s_down * M * H * 4;
@@ -103,9 +110,11 @@ static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
   take(L.x_out, (size_t)M * H * 4);
   take(L.mod, SL * 2 * 3 * H * 4);
   take(L.act, (size_t)d->layers * 4 * 4);
-  take(L.pk, (size_t)d->layers * d->prefix_len * d->head_dim * 2);
-  take(L.pv, (size_t)d->layers * d->prefix_len * d->head_dim * 2);
+  take(L.kc, (size_t)d->layers * L.kv_len * d->head_dim * 2);
+  take(L.vc, (size_t)d->layers * d->head_dim * L.ldv * 2);
   take(L.h, (size_t)M * H * 4);
+  take(L.q, L.qb);
+  take(L.aws, L.attn_ws);
   take(L.a_qkv, L.op_qkv);
   take(L.a_o, L.op_o);
   take(L.a_up, L.op_up);
@@ -121,10 +130,9 @@ static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
     take(L.d_a_o, SL * align256(L.op_o));
     take(L.d_a_up, SL * align256(L.op_up));
     take(L.d_a_down, SL * align256(L.op_down));
-    take(L.d_p_qkv, SL * align256(L.pq));
     take(L.d_p_o, SL * align256(L.po));
     take(L.d_p_down, SL * align256(L.pd));
-    take(L.d_qkv, SL * align256((size_t)M * L.nqkv * 2));
+    take(L.d_q, SL * align256(L.qb));
   }
   L.total = off;
   return FRT_OK;
@@ -176,10 +184,12 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
       uint8_t* a_o = dbg ? at(c, L.d_a_o, idx, align256(L.op_o)) : at(c, L.a_o);
       uint8_t* a_up = dbg ? at(c, L.d_a_up, idx, align256(L.op_up)) : at(c, L.a_up);
       uint8_t* a_down = dbg ? at(c, L.d_a_down, idx, align256(L.op_down)) : at(c, L.a_down);
-      float* p_qkv = dbg ? (float*)at(c, L.d_p_qkv, idx, align256(L.pq)) : (float*)at(c, L.p_qkv);
+      float* p_qkv = (float*)at(c, L.p_qkv);
       float* p_o = dbg ? (float*)at(c, L.d_p_o, idx, align256(L.po)) : (float*)at(c, L.p_o);
       float* p_down = dbg ? (float*)at(c, L.d_p_down, idx, align256(L.pd)) : (float*)at(c, L.p_down);
-      uint16_t* qkv_dbg = dbg ? (uint16_t*)at(c, L.d_qkv, idx, align256((size_t)M * L.nqkv * 2)) : nullptr;
+      uint16_t* qbuf = dbg ? (uint16_t*)at(c, L.d_q, idx, align256(L.qb)) : (uint16_t*)at(c, L.q);
+      uint16_t* kcl = (uint16_t*)at(c, L.kc) + (size_t)l * L.kv_len * d.head_dim;
+      uint16_t* vcl = (uint16_t*)at(c, L.vc) + (size_t)l * d.head_dim * L.ldv;
 
       // 1. producer: add the previous layer's MLP output, AdaRMSNorm (attention sublayer)
       RnqParams a{};
@@ -194,29 +204,35 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
       a.operand = a_qkv;
       FRT_HIP(launch_rnq(a, s)); ++n;
 
-      // 2. fused QKV GEMM -> partials
+      // 2. fused QKV GEMM: bf16 Q into its buffer, own K/V rows after the cached prefix
       GemmParams g{};
       g.M = M; g.MB = MB; g.ab_dtype = d.dtype; g.layout = FRT_W_PLAIN;
       g.N = L.nqkv; g.K = H; g.splits = L.s_qkv; g.ksteps_per_split = H / kstep_of(d.dtype) / L.s_qkv;
       g.a = a_qkv; g.w = (const uint8_t*)c->wq[l]; g.colscale = e4 ? c->sq[l] : nullptr;
-      g.act_scale = 1.f; g.act_scale_ptr = actp(l, SITE_QKV); g.partials = p_qkv; g.epi = FRT_EPI_NONE;
+      g.act_scale = 1.f; g.act_scale_ptr = actp(l, SITE_QKV); g.partials = p_qkv; g.epi = kEpiQkv;
+      g.q_out = qbuf; g.k_out = kcl + (size_t)d.prefix_len * d.head_dim;
+      g.v_out = vcl + d.prefix_len; g.v_ld = L.ldv; g.nq = L.nattn; g.hd = d.head_dim;
       FRT_HIP(launch_gemm(g, s)); ++n;
+      if (L.s_qkv > 1) {
+        ReduceParams r{};
+        r.M = M; r.N = L.nqkv; r.MB = MB; r.splits = L.s_qkv; r.partials = p_qkv;
+        r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_QKV); r.colscale = g.colscale; r.epi = kEpiQkv;
+        r.q_out = g.q_out; r.k_out = g.k_out; r.v_out = g.v_out; r.nq = g.nq; r.hd = g.hd; r.v_ld = g.v_ld;
+        FRT_HIP(launch_reduce(r, s)); ++n;
+      }
 
-      // 3. attention over the cached prefix -> O-projection operand
+      // 3. attention over [prefix ; own rows] -> O-projection operand
       AttnParams t{};
-      t.M = M; t.MB = MB; t.n_heads = d.n_heads; t.prefix_len = d.prefix_len;
-      t.qkv = p_qkv; t.splits = L.s_qkv; t.act_scale = 1.f; t.act_scale_ptr = actp(l, SITE_QKV);
-      t.colscale = e4 ? c->sq[l] : nullptr;
-      t.k_prefix = (const uint16_t*)at(c, L.pk) + (size_t)l * d.prefix_len * d.head_dim;
-      t.v_prefix = (const uint16_t*)at(c, L.pv) + (size_t)l * d.prefix_len * d.head_dim;
+      t.M = M; t.MB = MB; t.n_heads = d.n_heads; t.kv_len = L.kv_len;
+      t.q = qbuf; t.k = kcl; t.vt = vcl; t.ldv = L.ldv;
       t.out_dtype = d.dtype; t.out_scale = 1.f; t.out_scale_ptr = actp(l, SITE_O);
-      t.operand = a_o; t.qkv_out = qkv_dbg;
-      FRT_HIP(launch_attention(t, s)); ++n;
+      t.operand = a_o; t.workspace = (float*)at(c, L.aws);
+      FRT_HIP(launch_attention(t, s)); n += attention_kernel_count(L.kv_len);
 
       // 4. O projection -> partials
       g.N = H; g.K = L.nattn; g.splits = L.s_o; g.ksteps_per_split = L.nattn / kstep_of(d.dtype) / L.s_o;
       g.a = a_o; g.w = (const uint8_t*)c->wo[l]; g.colscale = e4 ? c->so[l] : nullptr;
-      g.act_scale_ptr = actp(l, SITE_O); g.partials = p_o;
+      g.act_scale_ptr = actp(l, SITE_O); g.partials = p_o; g.epi = FRT_EPI_NONE;
       FRT_HIP(launch_gemm(g, s)); ++n;
 
       // 5. producer: gated residual of the attention output, AdaRMSNorm (MLP sublayer)
@@ -346,7 +362,7 @@ extern "C" int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_de
     c->kernels = n;
   } else {
     // count the launches without enqueueing anything
-    const int per_layer = c->L.s_up == 1 ? 7 : 8;
+    const int per_layer = 6 + attention_kernel_count(c->L.kv_len) + (c->L.s_up > 1) + (c->L.s_qkv > 1);
     c->kernels = desc->steps * desc->layers * per_layer + 1;
   }
   *out = c;
@@ -358,10 +374,10 @@ extern "C" int frt_layer_chain_buffer(frt_chain* c, const char* name, void** dev
   const ChainLayout& L = c->L;
   struct Named { const char* n; const Buf* b; } tab[] = {
       {"x_in", &L.x_in}, {"x_out", &L.x_out}, {"mod", &L.mod}, {"act_scale", &L.act},
-      {"prefix_k", &L.pk}, {"prefix_v", &L.pv}, {"h", &L.h},
+      {"k_cache", &L.kc}, {"v_cache", &L.vc}, {"h", &L.h},
       {"dbg_h_attn", &L.d_h_attn}, {"dbg_h_mlp", &L.d_h_mlp}, {"dbg_a_qkv", &L.d_a_qkv},
       {"dbg_a_o", &L.d_a_o}, {"dbg_a_up", &L.d_a_up}, {"dbg_a_down", &L.d_a_down},
-      {"dbg_p_qkv", &L.d_p_qkv}, {"dbg_p_o", &L.d_p_o}, {"dbg_p_down", &L.d_p_down}, {"dbg_qkv", &L.d_qkv}};
+      {"dbg_p_o", &L.d_p_o}, {"dbg_p_down", &L.d_p_down}, {"dbg_q", &L.d_q}};
   for (const Named& t : tab) {
     if (strcmp(t.n, name) == 0) {
       if (t.b->bytes == 0) return FRT_E_STATE;

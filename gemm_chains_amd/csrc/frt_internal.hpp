@@ -146,6 +146,24 @@ __device__ __forceinline__ void store_operand4(uint8_t* op, int dtype, int MB, i
 
 __device__ __forceinline__ float load_scale(const float* p, float v) { return p ? __ldg(p) : v; }
 
+// Four consecutive columns n0..n0+3 of row m of a fused QKV output, rounded to bf16 and
+// written where attention reads them (the section boundaries are multiples of 16):
+// Q row-major [m][nq], K row-major [m][hd], V transposed v_out[d * v_ld + m].
+__device__ __forceinline__ void store_qkv4(uint16_t* q_out, uint16_t* k_out, uint16_t* v_out, int nq, int hd,
+                                           int v_ld, int m, int n0, f32x4 c) {
+  if (n0 < nq + hd) {
+    uint16_t* dst = n0 < nq ? q_out + (size_t)m * nq + n0 : k_out + (size_t)m * hd + (n0 - nq);
+    u32x2 w;
+    w.x = bf16_pack2(c.x, c.y);
+    w.y = bf16_pack2(c.z, c.w);
+    *reinterpret_cast<u32x2*>(dst) = w;
+  } else {
+    uint16_t* dst = v_out + (size_t)(n0 - nq - hd) * v_ld + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(size_t)r * v_ld] = (uint16_t)bf16_bits(c[r]);
+  }
+}
+
 // ------------------------------------------------------------------ kernel parameter blocks
 struct RnqParams {
   int M, K, MB;
@@ -182,6 +200,11 @@ struct GemmParams {
   int out_dtype;
   float out_scale;
   const float* out_scale_ptr;
+  // kEpiQkv: columns [0, nq) -> q_out[m][.], [nq, nq+hd) -> k_out[m][.], then V^T
+  uint16_t* q_out;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  int nq, hd, v_ld;
 };
 
 struct ReduceParams {
@@ -195,23 +218,31 @@ struct ReduceParams {
   int out_dtype;
   float out_scale;
   const float* out_scale_ptr;
+  uint16_t* q_out;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  int nq, hd, v_ld;
 };
 
 struct AttnParams {
-  int M, MB, n_heads, prefix_len;
-  const float* qkv;          // [splits][M][(n_heads+2)*128]
-  int splits;
-  float act_scale;
-  const float* act_scale_ptr;
-  const float* colscale;
-  const uint16_t* k_prefix;  // [prefix_len][128]
-  const uint16_t* v_prefix;
+  int M, MB, n_heads, kv_len;
+  const uint16_t* q;         // [M][n_heads*128] bf16
+  const uint16_t* k;         // [kv_len][128] bf16 (prefix rows, then the M own rows)
+  const uint16_t* vt;        // [128][ldv] bf16, V transposed (key index contiguous)
+  int ldv;                   // >= kv_len rounded up to 32
+  int chunk_keys;            // keys per workgroup (set by the launcher)
   int out_dtype;
   float out_scale;
   const float* out_scale_ptr;
   uint8_t* operand;
-  uint16_t* qkv_out;
+  float* workspace;          // chunk partial records when the key axis is split
 };
+
+// Epilogue codes used inside the library beyond the public frt_epilogue values.
+constexpr int kEpiQkv = 4;   // reduce + scale recovery + bf16, scattered into Q / K / V rows
+
+size_t attention_workspace_bytes(int M, int n_heads, int kv_len);
+int attention_kernel_count(int kv_len);
 
 // Launchers (stream-ordered, no validation: callers validate first).
 hipError_t launch_rnq(const RnqParams& p, hipStream_t s);
@@ -219,7 +250,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 // Library choices of split count and waves per workgroup.
-int choose_splits(int M, int N, int K, int dtype);
+int choose_splits(int M, int N, int K, int dtype, int epi);
 int choose_kwaves(int ksteps_per_split, int frags);
 
 }  // namespace frt

@@ -74,7 +74,9 @@ __device__ __forceinline__ void store_c4(const GemmParams& p, int m, int n0, f32
   if (m >= p.M) return;
   f32x4 c = v * as;
   if (p.colscale) c *= *reinterpret_cast<const f32x4*>(p.colscale + n0);
-  if (p.epi == FRT_EPI_STORE_F32) {
+  if (p.epi == kEpiQkv) {
+    store_qkv4(p.q_out, p.k_out, p.v_out, p.nq, p.hd, p.v_ld, m, n0, c);
+  } else if (p.epi == FRT_EPI_STORE_F32) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (size_t)m * p.N + n0) = c;
   } else {
     u32x2 w;
@@ -261,7 +263,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceParams p
     return;
   }
   const f32x4 c = reduce4(n0);
-  if (p.epi == FRT_EPI_STORE_F32) {
+  if (p.epi == kEpiQkv) {
+    store_qkv4(p.q_out, p.k_out, p.v_out, p.nq, p.hd, p.v_ld, m, n0, c);
+  } else if (p.epi == FRT_EPI_STORE_F32) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (size_t)m * p.N + n0) = c;
   } else {
     u32x2 w;
@@ -337,14 +341,18 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Split-K choice: enough workgroups to cover the 256 CUs, at most 4 K-chunks for wide
-// N (partials cost a write and a read of s*M*N*4 bytes), and chunks of >= 8 k-steps.
-int choose_splits(int M, int N, int K, int dtype) {
+// Split-K choice (measured on MI355X at the action-decoder shapes).  When the GEMM ends
+// in an epilogue, s > 1 costs a separate consumer kernel (~1.6 us of graph dispatch plus
+// its own memory round trip), more than the extra parallelism buys: s = 1.  When the
+// partials are the output (the next producer reduces them anyway), split until there are
+// two workgroups per CU (512) while every chunk keeps at least 4 k-steps.
+int choose_splits(int M, int N, int K, int dtype, int epi) {
   (void)M;
+  if (epi != FRT_EPI_NONE) return 1;
   const int tiles = N / 16;
   const int ksteps = K / kstep_of(dtype);
   int s = 1;
-  while (s < 16 && tiles * s < 256 && ksteps % (2 * s) == 0 && ksteps / (2 * s) >= 8) s *= 2;
+  while (s < 16 && tiles * s < 512 && ksteps % (2 * s) == 0 && ksteps / (2 * s) >= 4) s *= 2;
   return s;
 }
 
@@ -379,7 +387,7 @@ extern "C" int frt_splitk_choose(int M, int N, int K, int ab_dtype) {
   if (M < 1 || M > kMaxM || N < 16 || N % 16 || !is_ab_dtype(ab_dtype) || K < kstep_of(ab_dtype) ||
       K % kstep_of(ab_dtype))
     return 0;
-  return choose_splits(M, N, K, ab_dtype);
+  return choose_splits(M, N, K, ab_dtype, FRT_EPI_NONE);
 }
 
 extern "C" int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int splits, int ab_dtype,
@@ -395,7 +403,8 @@ extern "C" int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int spl
   FRT_CHECK(layout == FRT_W_PLAIN || layout == FRT_W_GATE_UP, FRT_E_ARG);
   if (layout == FRT_W_GATE_UP) FRT_CHECK(N % 32 == 0, FRT_E_SHAPE);
   FRT_CHECK(act_scale > 0.f && act_scale < __builtin_huge_valf(), FRT_E_ARG);
-  if (splits == 0) splits = choose_splits(M, N, K, ab_dtype);
+  FRT_CHECK(epi >= FRT_EPI_NONE && epi <= FRT_EPI_SILU_GATE_QUANT, FRT_E_ARG);
+  if (splits == 0) splits = choose_splits(M, N, K, ab_dtype, epi);
   FRT_CHECK(is_split(splits), FRT_E_SPLITK);
   const int ksteps = K / kstep_of(ab_dtype);
   FRT_CHECK(ksteps % splits == 0, FRT_E_SPLITK);
@@ -461,5 +470,64 @@ extern "C" int frt_splitk_reduce(void* stream, int M, int N, int splits, const f
   r.out = out_dev; r.out_dtype = out_dtype; r.out_scale = out_dtype == FRT_E4M3 ? out_act_scale : 1.f;
   r.out_scale_ptr = nullptr;
   FRT_HIP(launch_reduce(r, (hipStream_t)stream));
+  return FRT_OK;
+}
+
+extern "C" int frt_skinny_gemm_qkv(void* stream, int M, int K, int n_heads, int head_dim, int splits, int ab_dtype,
+                                   const void* a_packed_dev, const void* w_packed_dev, const float* w_colscale_dev,
+                                   float act_scale, float* partials_dev, size_t partials_bytes, uint16_t* q_out_dev,
+                                   uint16_t* k_out_dev, uint16_t* v_t_out_dev, int v_ld) {
+  uint16_t* v_out_dev = v_t_out_dev;
+  FRT_CHECK(a_packed_dev && w_packed_dev && q_out_dev && k_out_dev && v_out_dev, FRT_E_NULL);
+  FRT_CHECK(is_ab_dtype(ab_dtype), FRT_E_DTYPE);
+  FRT_CHECK(M >= 1 && M <= kMaxM, FRT_E_SHAPE);
+  FRT_CHECK(n_heads >= 1 && n_heads <= 64 && head_dim >= 16 && head_dim % 16 == 0, FRT_E_SHAPE);
+  FRT_CHECK(v_ld >= M, FRT_E_SHAPE);
+  const int N = (n_heads + 2) * head_dim;
+  FRT_CHECK(K >= kstep_of(ab_dtype) && K % kstep_of(ab_dtype) == 0 && K <= (1 << 16), FRT_E_SHAPE);
+  FRT_CHECK(act_scale > 0.f && act_scale < __builtin_huge_valf(), FRT_E_ARG);
+  if (splits == 0) splits = choose_splits(M, N, K, ab_dtype, kEpiQkv);
+  FRT_CHECK(is_split(splits), FRT_E_SPLITK);
+  const int ksteps = K / kstep_of(ab_dtype);
+  FRT_CHECK(ksteps % splits == 0, FRT_E_SPLITK);
+  const void* ptrs[] = {a_packed_dev, w_packed_dev, w_colscale_dev, partials_dev, q_out_dev, k_out_dev};
+  for (const void* q : ptrs) FRT_CHECK(aligned16(q), FRT_E_ALIGN);
+  FRT_CHECK(((uintptr_t)v_out_dev & 1u) == 0, FRT_E_ALIGN);  // V^T is written element by element
+  const size_t pbytes = (size_t)splits * M * N * 4;
+  if (splits > 1) {
+    FRT_CHECK(partials_dev, FRT_E_NULL);
+    FRT_CHECK(partials_bytes >= pbytes, FRT_E_WORKSPACE);
+  }
+  const size_t ab = frt_operand_bytes(ab_dtype, M, K), wb = frt_weight_bytes(ab_dtype, K, N);
+  const size_t qb = (size_t)M * n_heads * head_dim * 2, kb = (size_t)M * head_dim * 2;
+  const size_t vb = ((size_t)(head_dim - 1) * v_ld + M) * 2;
+  const void* outs[] = {q_out_dev, k_out_dev, v_out_dev};
+  const size_t outb[] = {qb, kb, vb};
+  for (int i = 0; i < 3; ++i) {
+    FRT_CHECK(!overlaps(outs[i], outb[i], a_packed_dev, ab), FRT_E_ALIAS);
+    FRT_CHECK(!overlaps(outs[i], outb[i], w_packed_dev, wb), FRT_E_ALIAS);
+    if (splits > 1) FRT_CHECK(!overlaps(outs[i], outb[i], partials_dev, pbytes), FRT_E_ALIAS);
+    for (int j = i + 1; j < 3; ++j) FRT_CHECK(!overlaps(outs[i], outb[i], outs[j], outb[j]), FRT_E_ALIAS);
+  }
+  if (splits > 1) {
+    FRT_CHECK(!overlaps(partials_dev, pbytes, a_packed_dev, ab), FRT_E_ALIAS);
+    FRT_CHECK(!overlaps(partials_dev, pbytes, w_packed_dev, wb), FRT_E_ALIAS);
+  }
+  GemmParams p{};
+  p.M = M; p.N = N; p.K = K; p.MB = m_blocks(M); p.splits = splits;
+  p.ab_dtype = ab_dtype; p.layout = FRT_W_PLAIN; p.ksteps_per_split = ksteps / splits;
+  p.a = (const uint8_t*)a_packed_dev; p.w = (const uint8_t*)w_packed_dev; p.colscale = w_colscale_dev;
+  p.act_scale = act_scale; p.act_scale_ptr = nullptr; p.partials = partials_dev; p.epi = kEpiQkv;
+  p.q_out = q_out_dev; p.k_out = k_out_dev; p.v_out = v_out_dev; p.nq = n_heads * head_dim; p.hd = head_dim;
+  p.v_ld = v_ld;
+  hipStream_t s = (hipStream_t)stream;
+  FRT_HIP(launch_gemm(p, s));
+  if (splits > 1) {
+    ReduceParams r{};
+    r.M = M; r.N = N; r.MB = p.MB; r.splits = splits; r.partials = partials_dev;
+    r.act_scale = act_scale; r.act_scale_ptr = nullptr; r.colscale = w_colscale_dev; r.epi = kEpiQkv;
+    r.q_out = q_out_dev; r.k_out = k_out_dev; r.v_out = v_out_dev; r.nq = p.nq; r.hd = head_dim; r.v_ld = v_ld;
+    FRT_HIP(launch_reduce(r, s));
+  }
   return FRT_OK;
 }

@@ -9,117 +9,80 @@
 // consumer reduces the FP32 partial sums); rebasdaily FlashRT-PAI news summary, section
 // "它优化的是“接力方式”" (the producer's output layout is exactly what the GEMM reads).
 //
-// One wave64 owns one row: each lane keeps K/64 values in registers (16 per 1024), the
-// sum of squares is reduced with a fixed butterfly (deterministic), and every lane writes
-// whole 16-byte slots of the packed operand.  Four rows per 256-thread workgroup; rows
-// M..Mp-1 write zero codes so the GEMM can always read full 16-row blocks.
+// One 256-thread workgroup owns one row (Mp workgroups), so a row's loads are spread over
+// four waves and issued together: each thread keeps groups of 4 consecutive k in
+// registers (one group per 1024 of K), the sum of squares is reduced with a fixed
+// butterfly inside each wave and then across the four waves in wave order (bitwise
+// deterministic), and each group is written as one 8-byte (bf16) or 4-byte (e4m3) piece of
+// a lane slot of the packed operand.  Rows M..Mp-1 write zero codes so the GEMM can always
+// read whole 16-row blocks.
 #include "frt_internal.hpp"
 
 namespace frt {
 
-constexpr int kRnqChunks = kMaxProducerK / (64 * 16);  // 16-element chunks per lane, max
+constexpr int kRnqGroups = kMaxProducerK / 1024;  // 4-element groups per thread, max
 
 __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int Mp = p.MB * 16;
-  if (m >= Mp) return;
-  const int nchunk = p.K >> 4;  // 16-element chunks in a row
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int K = p.K;
+  __shared__ float wsum[4];
   if (m >= p.M) {
-    if (p.operand) {
-      for (int c = lane; c < nchunk; c += 64)
-        for (int q = 0; q < 4; ++q)
-          store_operand4(p.operand, p.out_dtype, p.MB, m, c * 16 + 4 * q, 0.f, 0.f, 0.f, 0.f, 1.f, true);
+#pragma unroll
+    for (int i = 0; i < kRnqGroups; ++i) {
+      const int k0 = 4 * (tid + 256 * i);
+      if (k0 < K) store_operand4(p.operand, p.out_dtype, p.MB, m, k0, 0.f, 0.f, 0.f, 0.f, 1.f, true);
     }
     return;
   }
   const float xs = load_scale(p.x_scale_ptr, p.x_scale);
-  const size_t row = (size_t)m * p.K;
-  const size_t split_stride = (size_t)p.M * p.K;
+  const size_t row = (size_t)m * K;
+  const size_t split_stride = (size_t)p.M * K;
 
-  float h[kRnqChunks][16];
+  f32x4 h[kRnqGroups];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kRnqChunks; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= nchunk) break;
-    const int k0 = c * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 r = *reinterpret_cast<const f32x4*>(p.residual + row + k0 + 4 * q);
-      f32x4 hv = r;
-      if (p.x) {
-        f32x4 x = *reinterpret_cast<const f32x4*>(p.x + row + k0 + 4 * q);
-        for (int j = 1; j < p.x_splits; ++j) {
-          const f32x4 xj = *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0 + 4 * q);
-          x += xj;  // ascending split order
-        }
-        x *= xs;
-        if (p.x_colscale) x *= *reinterpret_cast<const f32x4*>(p.x_colscale + k0 + 4 * q);
-        if (p.gate) x *= *reinterpret_cast<const f32x4*>(p.gate + k0 + 4 * q);
-        hv = r + x;
-      }
-      if (p.residual_out) *reinterpret_cast<f32x4*>(p.residual_out + row + k0 + 4 * q) = hv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[i][4 * q + e] = hv[e];
-        ss = fmaf(hv[e], hv[e], ss);
-      }
+  for (int i = 0; i < kRnqGroups; ++i) {
+    const int k0 = 4 * (tid + 256 * i);
+    if (k0 >= K) break;
+    const f32x4 r = *reinterpret_cast<const f32x4*>(p.residual + row + k0);
+    f32x4 hv = r;
+    if (p.x) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(p.x + row + k0);
+      for (int j = 1; j < p.x_splits; ++j) x += *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
+      x *= xs;  // partials summed in ascending split order, then scale recovery
+      if (p.x_colscale) x *= *reinterpret_cast<const f32x4*>(p.x_colscale + k0);
+      if (p.gate) x *= *reinterpret_cast<const f32x4*>(p.gate + k0);
+      hv = r + x;
     }
+    if (p.residual_out) *reinterpret_cast<f32x4*>(p.residual_out + row + k0) = hv;
+    h[i] = hv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(hv[e], hv[e], ss);
   }
   if (!p.operand) return;
-  // wave-wide sum of squares, fixed butterfly order
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  const float inv = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+  if (lane == 0) wsum[wave] = ss;
+  __syncthreads();
+  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float inv = 1.0f / sqrtf(tot / (float)K + p.eps);
   const float as = load_scale(p.act_scale_ptr, p.act_scale);
-
 #pragma unroll
-  for (int i = 0; i < kRnqChunks; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= nchunk) break;
-    const int k0 = c * 16;
-    float y[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, sh = {0.f, 0.f, 0.f, 0.f};
-      if (p.ada_scale) sc = *reinterpret_cast<const f32x4*>(p.ada_scale + k0 + 4 * q);
-      if (p.ada_shift) sh = *reinterpret_cast<const f32x4*>(p.ada_shift + k0 + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float xh = h[i][4 * q + e] * inv;
-        float v = p.ada_scale ? xh * (1.0f + sc[e]) : xh;
-        if (p.ada_shift) v = v + sh[e];
-        y[4 * q + e] = v;
-      }
-    }
-    if (p.out_dtype == FRT_BF16) {
-      // 16 consecutive k = two 16-byte lane slots of the packed bf16 operand
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        u32x4 w;
-        w.x = bf16_pack2(y[8 * g + 0], y[8 * g + 1]);
-        w.y = bf16_pack2(y[8 * g + 2], y[8 * g + 3]);
-        w.z = bf16_pack2(y[8 * g + 4], y[8 * g + 5]);
-        w.w = bf16_pack2(y[8 * g + 6], y[8 * g + 7]);
-        *reinterpret_cast<u32x4*>(p.operand + operand_offset(FRT_BF16, p.MB, m, k0 + 8 * g)) = w;
-      }
-    } else {
-      // 16 consecutive k (16-aligned) = one 16-byte half slot of the packed e4m3 operand
-      u32x4 w;
-      w.x = e4m3_pack4(y[0] / as, y[1] / as, y[2] / as, y[3] / as);
-      w.y = e4m3_pack4(y[4] / as, y[5] / as, y[6] / as, y[7] / as);
-      w.z = e4m3_pack4(y[8] / as, y[9] / as, y[10] / as, y[11] / as);
-      w.w = e4m3_pack4(y[12] / as, y[13] / as, y[14] / as, y[15] / as);
-      *reinterpret_cast<u32x4*>(p.operand + operand_offset(FRT_E4M3, p.MB, m, k0)) = w;
-    }
+  for (int i = 0; i < kRnqGroups; ++i) {
+    const int k0 = 4 * (tid + 256 * i);
+    if (k0 >= K) break;
+    f32x4 y = h[i] * inv;
+    if (p.ada_scale) y = y * (1.0f + *reinterpret_cast<const f32x4*>(p.ada_scale + k0));
+    if (p.ada_shift) y = y + *reinterpret_cast<const f32x4*>(p.ada_shift + k0);
+    store_operand4(p.operand, p.out_dtype, p.MB, m, k0, y.x, y.y, y.z, y.w, as, false);
   }
 }
 
 hipError_t launch_rnq(const RnqParams& p, hipStream_t s) {
-  const int Mp = p.MB * 16;
-  const int rows = p.operand ? Mp : p.M;
-  hipLaunchKernelGGL(rnq_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, p);
+  const int rows = p.operand ? p.MB * 16 : p.M;
+  hipLaunchKernelGGL(rnq_kernel, dim3(rows), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

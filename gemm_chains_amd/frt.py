@@ -61,8 +61,11 @@ _SIGS = {
     "frt_splitk_reduce": (_int, [_c_void_p, _int, _int, _int, _c_void_p, _float, _c_void_p, _int, _c_void_p,
                                  _int, _float]),
     "frt_splitk_choose": (_int, [_int, _int, _int, _int]),
-    "frt_attention_prefix": (_int, [_c_void_p, _int, _int, _int, _int, _c_void_p, _int, _float, _c_void_p,
-                                    _c_void_p, _c_void_p, _int, _float, _c_void_p, _c_void_p]),
+    "frt_skinny_gemm_qkv": (_int, [_c_void_p, _int, _int, _int, _int, _int, _int, _c_void_p, _c_void_p, _c_void_p,
+                                   _float, _c_void_p, _size, _c_void_p, _c_void_p, _c_void_p, _int]),
+    "frt_attention_workspace_bytes": (_size, [_int, _int, _int, _int]),
+    "frt_attention_prefix": (_int, [_c_void_p, _int, _int, _int, _int, _c_void_p, _c_void_p, _c_void_p, _int,
+                                    _int, _float, _c_void_p, _c_void_p, _size]),
     "frt_layer_chain_arena_bytes": (_size, [ctypes.POINTER(ChainDesc)]),
     "frt_layer_chain_create": (_int, [ctypes.POINTER(ChainDesc), _c_void_p, _size, _c_void_p,
                                       ctypes.POINTER(_c_void_p)]),
@@ -198,12 +201,22 @@ def frt_splitk_reduce(M, N, splits, partials, act_scale, w_colscale, epi, out, o
                                     epi, _ptr(out), out_dtype, out_act_scale), "frt_splitk_reduce")
 
 
-def frt_attention_prefix(M, n_heads, head_dim, prefix_len, qkv_partials, qkv_splits, qkv_act_scale, qkv_colscale,
-                         k_prefix, v_prefix, out_dtype, out_act_scale, operand_out, qkv_out=None, stream=None):
-    _check(_lib().frt_attention_prefix(_stream(stream), M, n_heads, head_dim, prefix_len, _ptr(qkv_partials),
-                                       qkv_splits, qkv_act_scale, _ptr(qkv_colscale), _ptr(k_prefix),
-                                       _ptr(v_prefix), out_dtype, out_act_scale, _ptr(operand_out),
-                                       _ptr(qkv_out)), "frt_attention_prefix")
+def frt_skinny_gemm_qkv(M, K, n_heads, head_dim, splits, ab_dtype, a_packed, w_packed, w_colscale, act_scale,
+                        partials, partials_bytes, q_out, k_out, v_t_out, v_ld, stream=None):
+    _check(_lib().frt_skinny_gemm_qkv(_stream(stream), M, K, n_heads, head_dim, splits, ab_dtype, _ptr(a_packed),
+                                      _ptr(w_packed), _ptr(w_colscale), act_scale, _ptr(partials), partials_bytes,
+                                      _ptr(q_out), _ptr(k_out), _ptr(v_t_out), v_ld), "frt_skinny_gemm_qkv")
+
+
+def frt_attention_workspace_bytes(M, n_heads, head_dim, kv_len):
+    return _lib().frt_attention_workspace_bytes(M, n_heads, head_dim, kv_len)
+
+
+def frt_attention_prefix(M, n_heads, head_dim, kv_len, q, k, v_t, ldv, out_dtype, out_act_scale, operand_out,
+                         workspace, workspace_bytes, stream=None):
+    _check(_lib().frt_attention_prefix(_stream(stream), M, n_heads, head_dim, kv_len, _ptr(q), _ptr(k), _ptr(v_t),
+                                       ldv, out_dtype, out_act_scale, _ptr(operand_out), _ptr(workspace),
+                                       workspace_bytes), "frt_attention_prefix")
 
 
 # ------------------------------------------------------------------ chain

@@ -166,33 +166,55 @@ int frt_splitk_reduce(void* stream, int M, int N, int splits, const float* parti
                       float act_scale, const float* w_colscale_dev, int epi, void* out_dev,
                       int out_dtype, float out_act_scale);
 
-/* Library's split-K choice for a GEMM shape (what splits = 0 resolves to). */
+/* Library's split-K choice for a GEMM whose fp32 partials are its output (FRT_EPI_NONE;
+ * what splits = 0 resolves to there).  With an epilogue, splits = 0 resolves to 1: a
+ * split would cost a separate consumer kernel.  0 for an unsupported shape.            */
 int frt_splitk_choose(int M, int N, int K, int ab_dtype);
 
+/* Fused QKV projection: the skinny GEMM of a [Mp][K] operand with a packed weight of
+ * N = (n_heads + 2) * head_dim columns [Q | K | V] (three projections of one input merged
+ * into one wider GEMM: notes, section "CUDA Graph 与图化简分别省掉什么"), reduced (ascending
+ * split), scale-recovered (act_scale * w_colscale[n]) and rounded to bf16, then written
+ * straight where attention reads it: q_out_dev [M][n_heads*head_dim] and k_out_dev
+ * [M][head_dim] row-major; V transposed, v_t_out_dev[d * v_ld + m] (typically k_out_dev =
+ * row prefix_len of a key cache and v_t_out_dev = column prefix_len of a transposed value
+ * cache).  splits as for frt_skinny_gemm_splitk; partials_dev [splits][M][N] fp32 is
+ * needed only when splits resolves to more than 1.  head_dim % 16 == 0, v_ld >= M;
+ * v_t_out_dev needs only 2-byte alignment (it is written element by element).           */
+int frt_skinny_gemm_qkv(void* stream, int M, int K, int n_heads, int head_dim, int splits,
+                        int ab_dtype, const void* a_packed_dev, const void* w_packed_dev,
+                        const float* w_colscale_dev, float act_scale, float* partials_dev,
+                        size_t partials_bytes, uint16_t* q_out_dev, uint16_t* k_out_dev,
+                        uint16_t* v_t_out_dev, int v_ld);
+
 /* ------------------------------------------------------------------ attention */
-/* Attention of the M action rows over a cached prefix (one KV head shared by n_heads
- * query heads, no mask, scale 1/sqrt(head_dim)), fed straight from the fused QKV
- * GEMM's partials.  Not on the pages; it is the step between the QKV and O GEMMs of
- * the action-decoder layer.
- *   qkv = (sum_j qkv_partials[j]) * qkv_act_scale * qkv_colscale[n], columns
- *         [Q (n_heads*head_dim) | K (head_dim) | V (head_dim)], rounded to bf16;
- *   keys / values = [prefix (prefix_len rows, bf16) ; own K / V (M rows)];
+/* Attention of the M action rows over a cached key/value sequence: one KV head shared by
+ * n_heads query heads, no mask, scale 1/sqrt(head_dim).  Not on the pages; it is the
+ * step between the QKV and O GEMMs of the action-decoder layer.
+ *   q_dev [M][n_heads*head_dim] bf16; k_dev [kv_len][head_dim] bf16 (the cached prefix
+ *   followed by the M own rows, kv_len = prefix_len + M); v_t_dev [head_dim][ldv] bf16,
+ *   the values transposed (key index contiguous), ldv a multiple of 32 >= kv_len
+ *   (elements past kv_len are read but never used);
  *   O[m][h*d + e] = softmax_t(q_h . k_t / sqrt(d)) v_t[e], fp32-accurate;
  *   operand_out = packed bf16(O) or e4m3(O / out_act_scale), Mp x n_heads*head_dim.
- * qkv_out_dev: NULL, or [M][(n_heads+2)*head_dim] bf16 bits receiving the rounded Q/K/V.
- * head_dim == 128, 1 <= n_heads <= 16, 0 <= prefix_len <= 8192.                       */
-int frt_attention_prefix(void* stream, int M, int n_heads, int head_dim, int prefix_len,
-                         const float* qkv_partials_dev, int qkv_splits, float qkv_act_scale,
-                         const float* qkv_colscale_dev, const uint16_t* k_prefix_dev,
-                         const uint16_t* v_prefix_dev, int out_dtype, float out_act_scale,
-                         void* operand_out_dev, uint16_t* qkv_out_dev);
+ * Short sequences run as one workgroup per (head, 16-row block); long ones are cut into
+ * 256-key chunks whose FP32 partials (max, sum, unnormalised output) a second kernel
+ * merges in chunk order (deterministic).
+ * workspace_dev: frt_attention_workspace_bytes(...) bytes, no initial contents needed;
+ * calls that share a workspace must not overlap in time.
+ * head_dim == 128, 1 <= n_heads <= 16, M <= kv_len <= 8192 + 64.                        */
+size_t frt_attention_workspace_bytes(int M, int n_heads, int head_dim, int kv_len);
+int frt_attention_prefix(void* stream, int M, int n_heads, int head_dim, int kv_len,
+                         const uint16_t* q_dev, const uint16_t* k_dev, const uint16_t* v_t_dev,
+                         int ldv, int out_dtype, float out_act_scale, void* operand_out_dev,
+                         void* workspace_dev, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------ layer chain */
 /* One action-decoder layer (per layer l, per flow step k):
  *   h   = h + gate_mlp(prev) * x_mlp(prev)             (previous layer's MLP output)
  *   a   = quant(AdaRMSNorm(h; mod[k][l][0]))           producer
- *   qkv = a W_qkv[l]                                   GEMM (split-K)
- *   o   = quant(attention(qkv, prefix_k[l], prefix_v[l]))
+ *   q, k_cache[l][P..], v_cache[l][..][P..] = bf16(a W_qkv[l])   GEMM (split-K), own rows
+ *   o   = quant(attention(q, k_cache[l], v_cache[l]))  over prefix + own rows
  *   x   = o W_o[l];  h = h + mod[k][l][0].gate * x     GEMM, then producer
  *   b   = quant(AdaRMSNorm(h; mod[k][l][1]))
  *   z   = quant(SiLU(b W_gate) * (b W_up))             GEMM + fused consumer
@@ -237,13 +259,17 @@ int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_dev, size_t a
  *   "x_out"     [M][hidden] fp32   residual stream after the last layer of the last step
  *   "mod"       [steps][layers][2][3][hidden] fp32   (scale, shift, gate) per sublayer
  *   "act_scale" [layers][4] fp32   static activation scales (e4m3): qkv, o, up, down inputs
- *   "prefix_k", "prefix_v"  [layers][prefix_len][head_dim] bf16
+ *   "k_cache"   [layers][prefix_len + M][head_dim] bf16 and
+ *   "v_cache"   [layers][head_dim][ldv] bf16 (values transposed, ldv = prefix_len + M
+ *               rounded up to 32): the caller writes the prefix keys / values [0,
+ *               prefix_len); the entries after them are each layer's own rows, rewritten
+ *               by its QKV GEMM at every step
  *   "h"         [M][hidden] fp32   working residual stream (not kept per layer)
  *   debug (keep_intermediates): "dbg_h_attn", "dbg_h_mlp" [steps][layers][M][hidden] fp32,
  *   "dbg_a_qkv", "dbg_a_o", "dbg_a_up", "dbg_a_down" [steps][layers] packed operands,
- *   "dbg_p_qkv", "dbg_p_o", "dbg_p_down" [steps][layers][splits][M][N] fp32 and
- *   "dbg_qkv" [steps][layers][M][(n_heads+2)*head_dim] bf16; each (step, layer) slice
- *   starts on a 256-byte boundary.  A name whose buffer is empty returns FRT_E_STATE. */
+ *   "dbg_p_o", "dbg_p_down" [steps][layers][splits][M][N] fp32 and "dbg_q"
+ *   [steps][layers][M][n_heads*head_dim] bf16; each (step, layer) slice starts on a
+ *   256-byte boundary.  A name whose buffer is empty returns FRT_E_STATE.              */
 int frt_layer_chain_buffer(frt_chain* chain, const char* name, void** dev, size_t* bytes);
 /* Run every step and layer once on `stream` (one hipGraphLaunch, or eager launches). */
 int frt_layer_chain_run(frt_chain* chain, void* stream);

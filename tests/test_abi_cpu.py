@@ -166,20 +166,39 @@ def test_gemm_validation():
 @no_gpu
 def test_attention_and_pack_validation():
     f = "frt_attention_prefix"
-    base = [None, 50, 8, 128, 800, FAKE, 1, 1.0, None, FAKE + (1 << 30), FAKE + (2 << 30), frt.BF16, 1.0,
-            FAKE + (3 << 30), None]
+    ws = frt.frt_attention_workspace_bytes(50, 8, 128, 850)
+    assert ws > 0 and frt.frt_attention_workspace_bytes(50, 8, 64, 850) == 0
+    base = [None, 50, 8, 128, 850, FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 864, frt.BF16, 1.0,
+            FAKE + (3 << 30), FAKE + (4 << 30), ws]
     def call(**kw):
         a = list(base)
         for i, v in kw.items():
             a[int(i[1:])] = v
         return _st(f, *a)
-    assert call(a5=None) == frt.E_NULL
-    assert call(a9=None) == frt.E_NULL
+    assert call(a5=None) == frt.E_NULL and call(a12=None) == frt.E_NULL
     assert call(a3=64) == frt.E_SHAPE and call(a2=0) == frt.E_SHAPE and call(a4=9000) == frt.E_SHAPE
-    assert call(a6=0) == frt.E_SPLITK
-    assert call(a11=5) == frt.E_DTYPE
-    assert call(a7=-1.0) == frt.E_ARG
-    assert call(a13=FAKE) == frt.E_ALIAS
+    assert call(a4=49) == frt.E_SHAPE                        # kv_len must cover the M own rows
+    assert call(a8=850) == frt.E_SHAPE and call(a8=832) == frt.E_SHAPE   # ldv: multiple of 32 >= kv_len
+    assert call(a9=5) == frt.E_DTYPE
+    assert call(a9=frt.E4M3, a10=-1.0) == frt.E_ARG
+    if ws > 16:
+        assert call(a13=ws - 1) == frt.E_WORKSPACE
+    assert call(a11=FAKE) == frt.E_ALIAS
+    assert call(a6=FAKE + 8) == frt.E_ALIGN
+    qf = "frt_skinny_gemm_qkv"
+    qbase = [None, 50, 1024, 8, 128, 1, frt.BF16, FAKE, FAKE + (1 << 30), None, 1.0, None, 0,
+             FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30), 864]
+    def qcall(**kw):
+        a = list(qbase)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return _st(qf, *a)
+    assert qcall(a13=None) == frt.E_NULL
+    assert qcall(a4=100) == frt.E_SHAPE
+    assert qcall(a5=4) == frt.E_NULL                         # split needs partials
+    assert qcall(a5=4, a11=FAKE + (5 << 30), a12=10) == frt.E_WORKSPACE
+    assert qcall(a14=FAKE + (2 << 30) + 64) == frt.E_ALIAS    # K rows overlap the Q rows
+    assert qcall(a16=10) == frt.E_SHAPE                        # V^T rows shorter than M
     g = "frt_pack_weight"
     assert _st(g, None, 1024, 1024, None, None, frt.BF16, 0, FAKE, None) == frt.E_NULL
     assert _st(g, None, 1000, 1024, FAKE, None, frt.BF16, 0, FAKE + (1 << 30), None) == frt.E_SHAPE

@@ -261,42 +261,66 @@ def test_gemm_silu_gate_epilogue(F, M, N, K, dtype, splits):
     assert np.all(codes[M:] == 0)
 
 
-# ------------------------------------------------------------------ attention
+# ------------------------------------------------------------------ fused QKV GEMM
 
-def _dyadic(seed, shape, scale_bits=10):
-    """Values k * 2^-scale_bits with |k| < 2^12: float32 sums of up to 16 stay exact."""
-    g = np.random.default_rng(seed)
-    return (g.integers(-2 ** 11, 2 ** 11, size=shape) * 2.0 ** -scale_bits).astype(np.float32)
-
-
-@pytest.mark.parametrize("M,splits,out_dtype,prefix,colscale", [
-    (50, 4, "bf16", 800, False), (10, 1, "e4m3", 800, True), (50, 2, "e4m3", 800, True),
-    (1, 1, "bf16", 0, False), (64, 8, "bf16", 37, False), (17, 1, "bf16", 800, False)])
-def test_attention_parity(F, M, splits, out_dtype, prefix, colscale):
+@pytest.mark.parametrize("M,K,dtype,splits", [(50, 1024, "bf16", 1), (50, 1024, "bf16", 4), (10, 1024, "e4m3", 1),
+                                              (10, 1024, "e4m3", 2), (64, 2048, "bf16", 2), (1, 128, "e4m3", 1)])
+def test_qkv_gemm_epilogue(F, M, K, dtype, splits):
     frt, dev = F
     nh, hd = 8, 128
-    nqkv = (nh + 2) * hd
-    dt = frt.DTYPES[out_dtype]
-    parts = _dyadic(M + splits, (splits, M, nqkv)) / np.float32(splits)
-    act = 0.5 if colscale else 1.0
-    cs = (2.0 ** np.random.default_rng(3).integers(-2, 2, nqkv)).astype(np.float32) if colscale else None
-    kp = synth.to_bf16_bits(synth.normal(3, 94, 0, (prefix, hd))) if prefix else np.zeros((0, hd), np.uint16)
-    vp = synth.to_bf16_bits(synth.normal(3, 94, 1, (prefix, hd))) if prefix else np.zeros((0, hd), np.uint16)
-    c = ref.reduce_partials(parts, act, cs)
-    o_full = ref.attention_block(c, codec.bf16_decode(kp), codec.bf16_decode(vp), nh, hd, out_dtype, 1.0)
-    out_scale = float(np.float32(np.max(np.abs(o_full["o"])) / 448.0)) if out_dtype == "e4m3" else 1.0
-    o = ref.attention_block(c, codec.bf16_decode(kp), codec.bf16_decode(vp), nh, hd, out_dtype, out_scale)
-    op = dev.empty_bytes(frt.frt_operand_bytes(dt, M, nh * hd))
-    qkv_out = torch.empty((M, nqkv), dtype=torch.int16, device="cuda")
-    kp_t = dev.to_dev(_i16(kp)) if prefix else None
-    vp_t = dev.to_dev(_i16(vp)) if prefix else None
-    frt.frt_attention_prefix(M, nh, hd, prefix, dev.to_dev(parts), splits, act, dev.to_dev(cs) if colscale else None,
-                             kp_t, vp_t, dt, out_scale, op, qkv_out)
+    N = (nh + 2) * hd
+    dt, a_pk, w_pk, a_dec, w_dec, s_w = _gemm_inputs(frt, dev, M, N, K, dtype, seed=21 + M + K)
+    act = 0.0625 if dtype == "e4m3" else 1.0
+    cs = dev.to_dev(s_w.astype(np.float32)) if dtype == "e4m3" else None
+    c_o = ref.reduce_partials(ref.gemm_splitk(a_dec, w_dec, 1), act, s_w)
+    g_mag = (np.abs(a_dec) @ np.abs(w_dec)) * act * (s_w[None, :] if s_w is not None else 1.0)
+    qo = torch.zeros((M, nh * hd), dtype=torch.int16, device="cuda")
+    kc = torch.zeros((M + 3, hd), dtype=torch.int16, device="cuda")      # rows 3.. as in a key cache
+    ldv = (M + 3 + 31) // 32 * 32
+    vc = torch.zeros((hd, ldv), dtype=torch.int16, device="cuda")        # transposed value cache
+    parts = dev.empty_f32(splits, M, N) if splits > 1 else None
+    frt.frt_skinny_gemm_qkv(M, K, nh, hd, splits, dt, a_pk, w_pk, cs, act, parts,
+                            0 if parts is None else parts.numel() * 4, qo, kc[3:], vc[:, 3:], ldv)
     torch.cuda.synchronize()
-    q_bits = _u16(qkv_out)
-    want_q = codec.bf16_encode(np.concatenate([o["q"], o["k"], o["v_own"]], axis=1))
-    assert np.array_equal(q_bits, want_q), "exact inputs: Q/K/V bf16 codes must match bit for bit"
+    got = np.concatenate([_u16(qo), _u16(kc[3:]), _u16(vc[:, 3:3 + M]).T], axis=1)
+    check_codes(got, c_o, g_mag, "bf16", max_frac=0.01 if dtype == "bf16" else 0.05, label=f"qkv {dtype} s={splits}")
+    assert np.all(_u16(kc[:3]) == 0) and np.all(_u16(vc[:, :3]) == 0) and np.all(_u16(vc[:, 3 + M:]) == 0), \
+        "cache entries outside the own rows are left untouched"
+
+
+# ------------------------------------------------------------------ attention
+
+@pytest.mark.parametrize("M,out_dtype,prefix", [(50, "bf16", 800), (10, "e4m3", 800), (50, "e4m3", 800),
+                                                (1, "bf16", 0), (64, "bf16", 37), (17, "bf16", 800),
+                                                (50, "bf16", 2000), (10, "bf16", 127), (3, "bf16", 8190)])
+def test_attention_parity(F, M, out_dtype, prefix):
+    frt, dev = F
+    nh, hd = 8, 128
+    T = prefix + M
+    dt = frt.DTYPES[out_dtype]
+    qb = synth.to_bf16_bits(synth.normal(M + prefix, 94, 0, (M, nh * hd)))
+    kb = synth.to_bf16_bits(synth.normal(M + prefix, 94, 1, (T, hd)))
+    vb = synth.to_bf16_bits(synth.normal(M + prefix, 94, 2, (T, hd)))
+    o, mag = ref.attention_prefix(codec.bf16_decode(qb), codec.bf16_decode(kb), codec.bf16_decode(vb), nh, hd)
+    out_scale = float(np.float32(np.max(np.abs(o)) / 448.0)) if out_dtype == "e4m3" else 1.0
+    v, _, _ = ref.quantise(o, out_dtype, out_scale)
+    if out_dtype == "e4m3":
+        mag = mag / out_scale
+    wsb = frt.frt_attention_workspace_bytes(M, nh, hd, T)
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda")   # no initial contents needed
+    ldv = (T + 31) // 32 * 32
+    vt = np.full((hd, ldv), 0x7FC0, np.uint16)                        # padding holds NaN: never used
+    vt[:, :T] = vb.T
+    ops = []
+    for _ in range(2):                       # the second call reuses the workspace as left by the first
+        op = dev.empty_bytes(frt.frt_operand_bytes(dt, M, nh * hd))
+        op.fill_(0xAB)
+        frt.frt_attention_prefix(M, nh, hd, T, dev.to_dev(_i16(qb)), dev.to_dev(_i16(kb)), dev.to_dev(_i16(vt)),
+                                 ldv, dt, out_scale, op, ws, wsb)
+        ops.append(op)
+    torch.cuda.synchronize()
     Mp = 16 * math.ceil(M / 16)
-    codes = dev.operand_codes(op, dt, Mp, nh * hd)
-    check_codes(codes[:M], o["v"], o["mag"], out_dtype, label=f"attention {out_dtype} M={M}")
+    codes = dev.operand_codes(ops[0], dt, Mp, nh * hd)
+    check_codes(codes[:M], v, mag, out_dtype, label=f"attention {out_dtype} M={M} T={T}")
     assert np.all(codes[M:] == 0)
+    assert torch.equal(ops[0], ops[1]), "repeat call must be bit-identical"
