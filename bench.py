@@ -145,6 +145,7 @@ def main():
               "one-device latency path (see the design notes on sharding); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import synth
     from gemm_chains_amd import chain, device, frt
@@ -156,22 +157,44 @@ def main():
         dims = synth.chain_dims(layers=args.layers, steps=args.flow_steps, M=M)
         log(f"M={M}: generating {dims['layers']}-layer weights and inputs")
         wl = synth.workload4(dims)
-        packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
-        ch = chain.Chain(dims, packed, use_graph=True)
-        chain.load_workload(ch, wl)
-        torch.cuda.synchronize()
-        log(f"M={M}: {ch.kernel_count()} kernels per decision; timing {args.steps} decisions")
-        ms = time_chain(torch, ch, args.steps, args.warmup)
         nl = dims["layers"] * dims["steps"]
-        wb = chain_weight_bytes(dims, 2)
-        results[M] = dict(ms=ms, us_layer=ms * 1e3 / nl, kernels=ch.kernel_count(),
-                          weight_gbs=(wb * dims["steps"] + kv_bytes(dims) * dims["steps"]) / (ms * 1e-3) / 1e9,
-                          dims=dims)
-        log(f"M={M}: {ms:.3f} ms/decision, {results[M]['us_layer']:.2f} us/layer, "
-            f"{results[M]['weight_gbs']:.0f} GB/s weights+KV")
+        packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
+        variants = [("bf16", False), ("bf16", True)] if M == 50 else [("bf16", False)]
+        for dt_name, pf in variants:  # M=50: paired ablation of the weight-prefetch branch
+            ch = chain.Chain(dims, packed, use_graph=True, prefetch_next=pf)
+            chain.load_workload(ch, wl)
+            torch.cuda.synchronize()
+            ms = time_chain(torch, ch, args.steps, args.warmup)
+            wb = chain_weight_bytes(dims, 2)
+            results[(M, dt_name, pf)] = dict(
+                ms=ms, us_layer=ms * 1e3 / nl, kernels=ch.kernel_count(), dims=dims,
+                weight_gbs=(wb + kv_bytes(dims)) * dims["steps"] / (ms * 1e-3) / 1e9)
+            log(f"M={M} {dt_name} prefetch={int(pf)}: {ch.kernel_count()} kernels, {ms:.3f} ms/decision, "
+                f"{ms * 1e3 / nl:.2f} us/layer")
+            ch.close()
+        # e4m3 chain: static activation scales from one bf16 run on the calibration inputs
+        x0c, modc = synth.chain_inputs(dims, synth.CAL_SEED)
+        cal = chain.Chain(dims, packed, use_graph=False)
+        chain.load_workload(cal, dict(wl, x0=x0c, mod=modc))
+        scales = cal.calibrate().cpu().numpy()
+        cal.close()
+        del packed
+        packed8 = chain.PackedLayers(wl["layers"], dims, frt.E4M3)
+        ch = chain.Chain(dims, packed8, use_graph=True)
+        chain.load_workload(ch, wl, scales)
+        torch.cuda.synchronize()
+        ms = time_chain(torch, ch, args.steps, args.warmup)
+        wb = chain_weight_bytes(dims, 1) + dims["layers"] * 4 * (1280 + 1024 + 8192 + 1024)
+        results[(M, "e4m3", False)] = dict(ms=ms, us_layer=ms * 1e3 / nl, kernels=ch.kernel_count(), dims=dims,
+                                           weight_gbs=(wb + kv_bytes(dims)) * dims["steps"] / (ms * 1e-3) / 1e9,
+                                           finite=bool(np.isfinite(ch.read("x_out")).all()))
+        log(f"M={M} e4m3: {ms:.3f} ms/decision, {ms * 1e3 / nl:.2f} us/layer")
         ch.close()
-        del packed, wl
+        del packed8, wl
         torch.cuda.empty_cache()
+    best_pf = results[(50, "bf16", True)]["ms"] < results[(50, "bf16", False)]["ms"]
+    results[50] = results[(50, "bf16", best_pf)]
+    results[10] = results[(10, "bf16", False)]
 
     dims50 = results[50]["dims"]
     us, nbytes, splits = time_dominant_gemm(torch, frt, device, synth, dims50, frt.BF16)
@@ -201,7 +224,14 @@ def main():
         "config": {"workload": "action-decoder chain, 18 layers x 10 flow steps, M=50, hidden 1024, "
                                "8 q heads / 1 kv head x 128, 800-token prefix, MLP 4096, bf16, hipGraph replay",
                    "layers": dims50["layers"], "flow_steps": dims50["steps"], "M": 50,
-                   "kernels_per_decision": r["kernels"]},
+                   "kernels_per_decision": r["kernels"], "weight_prefetch_branch": best_pf},
+        "ablation_prefetch": {"us_per_layer_m50_off": round(results[(50, "bf16", False)]["us_layer"], 3),
+                              "us_per_layer_m50_on": round(results[(50, "bf16", True)]["us_layer"], 3)},
+        "e4m3": {"us_per_layer_m50": round(results[(50, "e4m3", False)]["us_layer"], 3),
+                 "us_per_layer_m10": round(results[(10, "e4m3", False)]["us_layer"], 3),
+                 "weight_stream_gbs_m50": round(results[(50, "e4m3", False)]["weight_gbs"], 1),
+                 "scales": "calibrated on the GPU (one bf16 run on seed-1 inputs)",
+                 "outputs_finite": results[(50, "e4m3", False)]["finite"] and results[(10, "e4m3", False)]["finite"]},
         "us_per_layer_m10": round(results[10]["us_layer"], 3),
         "ms_per_decision_m10": round(results[10]["ms"], 4),
         "weight_stream_gbs": round(r["weight_gbs"], 1),

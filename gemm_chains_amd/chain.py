@@ -35,7 +35,7 @@ class Chain:
     """One chain handle with its own arena (a torch uint8 CUDA tensor)."""
 
     def __init__(self, dims, packed, splits=(0, 0, 0, 0), use_graph=True, keep_intermediates=False, eps=1e-6,
-                 stream=None):
+                 stream=None, prefetch_next=False):
         e4 = packed.dtype == frt.E4M3
         self.dims = dims
         self.desc, self._keep = frt.make_chain_desc(
@@ -44,7 +44,7 @@ class Chain:
             packed.w["qkv"], packed.w["o"], packed.w["up"], packed.w["down"],
             packed.s["qkv"] if e4 else None, packed.s["o"] if e4 else None,
             packed.s["up"] if e4 else None, packed.s["down"] if e4 else None,
-            use_graph=use_graph, keep_intermediates=keep_intermediates)
+            use_graph=use_graph, keep_intermediates=keep_intermediates, prefetch_next=prefetch_next)
         self.packed = packed
         nbytes = frt.frt_layer_chain_arena_bytes(self.desc)
         if nbytes == 0:
@@ -70,6 +70,12 @@ class Chain:
 
     def run(self, stream=None):
         frt.frt_layer_chain_run(self.handle, stream)
+
+    def calibrate(self, stream=None):
+        """Static e4m3 activation scales [layers][4] from one recorded bf16 run (device tensor)."""
+        out = torch.empty((self.dims["layers"], 4), dtype=torch.float32, device=device.DEV)
+        frt.frt_layer_chain_calibrate(self.handle, out, stream)
+        return out
 
     def kernel_count(self):
         return frt.frt_layer_chain_kernel_count(self.handle)

@@ -241,6 +241,7 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
     if (nch == 1) {
       const f32x4 ov = acc / den;
       store_operand4(p.operand, p.out_dtype, MB, m, h * HD + d, ov.x, ov.y, ov.z, ov.w, os, m >= M);
+      if (m < M) record_amax(p.amax, ov.x, ov.y, ov.z, ov.w);
     } else {
       *reinterpret_cast<f32x4*>(rec + 32 + tq * HD + d) = acc;
     }
@@ -283,6 +284,10 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
                  m >= p.M);
   store_operand4(p.operand, p.out_dtype, MB, m, k + 4, num[4] / den, num[5] / den, num[6] / den, num[7] / den, os,
                  m >= p.M);
+  if (m < p.M) {
+    record_amax(p.amax, num[0] / den, num[1] / den, num[2] / den, num[3] / den);
+    record_amax(p.amax, num[4] / den, num[5] / den, num[6] / den, num[7] / den);
+  }
 }
 
 hipError_t launch_attention(const AttnParams& p_in, hipStream_t s) {

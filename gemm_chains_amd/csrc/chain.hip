@@ -19,6 +19,32 @@
 namespace frt {
 
 enum { SITE_QKV = 0, SITE_O = 1, SITE_UP = 2, SITE_DOWN = 3 };
+
+// Reads a layer's four packed weights (and nothing else) so that they sit in the
+// last-level cache when the layer's GEMMs stream them.  Runs on a concurrent graph
+// branch with a small grid; the loaded data is folded into a value that is never stored.
+struct PrefetchParams {
+  const u32x4* w[4];
+  size_t n16[4];  // 16-byte units
+  unsigned* sink;
+};
+__global__ void __launch_bounds__(256) prefetch_kernel(const PrefetchParams p) {
+  unsigned acc = 0;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const u32x4* w = p.w[m];
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.n16[m]; i += 4 * stride) {
+      u32x4 a = w[i];
+      u32x4 b = i + stride < p.n16[m] ? w[i + stride] : a;
+      u32x4 c = i + 2 * stride < p.n16[m] ? w[i + 2 * stride] : a;
+      u32x4 d = i + 3 * stride < p.n16[m] ? w[i + 3 * stride] : a;
+      acc ^= a.x ^ b.y ^ c.z ^ d.w;
+    }
+  }
+  if (acc == 0x9e3779b9u && p.sink) *p.sink = acc;  // keeps the loads; practically never taken
+}
+constexpr int kPrefetchBlocks = 64;
 enum { MOD_SCALE = 0, MOD_SHIFT = 1, MOD_GATE = 2 };
 
 struct Buf {
@@ -33,7 +59,7 @@ struct ChainLayout {
   size_t op_qkv = 0, op_o = 0, op_up = 0, op_down = 0;     // operand bytes
   size_t pq = 0, po = 0, pu = 0, pd = 0;                   // partial bytes (one copy)
   size_t qb = 0, attn_ws = 0;
-  Buf x_in, x_out, mod, act, kc, vc, h, q, aws, a_qkv, a_o, a_up, a_down, p_qkv, p_o, p_up, p_down;
+  Buf x_in, x_out, mod, act, kc, vc, h, q, aws, sink, amax, a_qkv, a_o, a_up, a_down, p_qkv, p_o, p_up, p_down;
   Buf d_h_attn, d_h_mlp, d_a_qkv, d_a_o, d_a_up, d_a_down, d_p_o, d_p_down, d_q;
   size_t total = 0;
 };
@@ -115,6 +141,8 @@ static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
   take(L.h, (size_t)M * H * 4);
   take(L.q, L.qb);
   take(L.aws, L.attn_ws);
+  take(L.sink, 64);
+  take(L.amax, (size_t)d->layers * 4 * 4);
   take(L.a_qkv, L.op_qkv);
   take(L.a_o, L.op_o);
   take(L.a_up, L.op_up);
@@ -159,7 +187,28 @@ static uint8_t* at(frt_chain* c, const Buf& b, size_t idx = 0, size_t stride = 0
 }
 
 // Enqueue the whole chain on `s` (eager launches; also what graph capture records).
-static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
+static int enqueue_prefetch(frt_chain* c, int l, hipStream_t side) {
+  const frt_chain_desc& d = c->d;
+  const int ks = d.dtype == FRT_BF16 ? 2 : 1;
+  const int H = d.hidden, F = d.mlp, nq = d.n_heads * d.head_dim, nqkv = nq + 2 * d.head_dim;
+  PrefetchParams p{};
+  const void* w[4] = {c->wq[l], c->wo[l], c->wu[l], c->wd[l]};
+  const size_t bytes[4] = {(size_t)H * nqkv * ks, (size_t)nq * H * ks, (size_t)H * 2 * F * ks, (size_t)F * H * ks};
+  for (int i = 0; i < 4; ++i) {
+    p.w[i] = (const u32x4*)w[i];
+    p.n16[i] = bytes[i] / 16;
+  }
+  p.sink = (unsigned*)at(c, c->L.sink);
+  hipLaunchKernelGGL(prefetch_kernel, dim3(kPrefetchBlocks), dim3(256), 0, side, p);
+  FRT_HIP(hipGetLastError());
+  return FRT_OK;
+}
+
+// side / fork / join: when given (graph capture with prefetch_next), layer l's first
+// kernel is followed by an event that a side stream waits on before reading the weights
+// of the layer after l; the side stream rejoins the main stream at the end.
+static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, hipStream_t side = nullptr,
+                         hipEvent_t* evs = nullptr, unsigned* amax = nullptr) {
   const frt_chain_desc& d = c->d;
   const ChainLayout& L = c->L;
   const int M = d.M, H = d.hidden, F = d.mlp, MB = m_blocks(M);
@@ -202,7 +251,18 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
       a.ada_scale = modp(k, l, 0, MOD_SCALE); a.ada_shift = modp(k, l, 0, MOD_SHIFT);
       a.eps = d.eps; a.out_dtype = d.dtype; a.act_scale = 1.f; a.act_scale_ptr = actp(l, SITE_QKV);
       a.operand = a_qkv;
+      a.amax = amax ? amax + l * 4 + SITE_QKV : nullptr;
       FRT_HIP(launch_rnq(a, s)); ++n;
+      if (side) {  // prefetch the next layer in chain order while this one runs
+        const int idx_next = k * d.layers + l + 1;
+        if (idx_next < d.steps * d.layers) {
+          FRT_HIP(hipEventRecord(evs[idx_next], s));
+          FRT_HIP(hipStreamWaitEvent(side, evs[idx_next], 0));
+          int rc = enqueue_prefetch(c, idx_next % d.layers, side);
+          if (rc != FRT_OK) return rc;
+          ++n;
+        }
+      }
 
       // 2. fused QKV GEMM: bf16 Q into its buffer, own K/V rows after the cached prefix
       GemmParams g{};
@@ -227,12 +287,13 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
       t.q = qbuf; t.k = kcl; t.vt = vcl; t.ldv = L.ldv;
       t.out_dtype = d.dtype; t.out_scale = 1.f; t.out_scale_ptr = actp(l, SITE_O);
       t.operand = a_o; t.workspace = (float*)at(c, L.aws);
+      t.amax = amax ? amax + l * 4 + SITE_O : nullptr;
       FRT_HIP(launch_attention(t, s)); n += attention_kernel_count(L.kv_len);
 
       // 4. O projection -> partials
       g.N = H; g.K = L.nattn; g.splits = L.s_o; g.ksteps_per_split = L.nattn / kstep_of(d.dtype) / L.s_o;
       g.a = a_o; g.w = (const uint8_t*)c->wo[l]; g.colscale = e4 ? c->so[l] : nullptr;
-      g.act_scale_ptr = actp(l, SITE_O); g.partials = p_o; g.epi = FRT_EPI_NONE;
+      g.act_scale_ptr = actp(l, SITE_O); g.partials = p_o; g.epi = FRT_EPI_NONE; g.amax = nullptr;
       FRT_HIP(launch_gemm(g, s)); ++n;
 
       // 5. producer: gated residual of the attention output, AdaRMSNorm (MLP sublayer)
@@ -242,6 +303,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
       b.residual = h_attn; b.residual_out = h_mlp; b.gate = modp(k, l, 0, MOD_GATE);
       b.ada_scale = modp(k, l, 1, MOD_SCALE); b.ada_shift = modp(k, l, 1, MOD_SHIFT);
       b.act_scale_ptr = actp(l, SITE_UP); b.operand = a_up;
+      b.amax = amax ? amax + l * 4 + SITE_UP : nullptr;
       FRT_HIP(launch_rnq(b, s)); ++n;
 
       // 6. gate|up GEMM with SiLU(gate)*up + quantise (fused when not split)
@@ -249,6 +311,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
       g.layout = FRT_W_GATE_UP; g.a = a_up; g.w = (const uint8_t*)c->wu[l]; g.colscale = e4 ? c->su[l] : nullptr;
       g.act_scale_ptr = actp(l, SITE_UP);
       g.out_dtype = d.dtype; g.out_scale = 1.f; g.out_scale_ptr = actp(l, SITE_DOWN);
+      g.amax = amax ? amax + l * 4 + SITE_DOWN : nullptr;
       if (L.s_up == 1) {
         g.epi = FRT_EPI_SILU_GATE_QUANT; g.out = a_down; g.partials = nullptr;
         FRT_HIP(launch_gemm(g, s)); ++n;
@@ -259,7 +322,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
         r.M = M; r.N = 2 * F; r.MB = MB; r.splits = L.s_up; r.partials = g.partials;
         r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_UP); r.colscale = g.colscale;
         r.epi = FRT_EPI_SILU_GATE_QUANT; r.out = a_down; r.out_dtype = d.dtype; r.out_scale = 1.f;
-        r.out_scale_ptr = actp(l, SITE_DOWN);
+        r.out_scale_ptr = actp(l, SITE_DOWN); r.amax = g.amax;
         FRT_HIP(launch_reduce(r, s)); ++n;
       }
 
@@ -267,6 +330,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count) {
       g.N = H; g.K = F; g.splits = L.s_down; g.ksteps_per_split = F / kstep_of(d.dtype) / L.s_down;
       g.layout = FRT_W_PLAIN; g.a = a_down; g.w = (const uint8_t*)c->wd[l]; g.colscale = e4 ? c->sd[l] : nullptr;
       g.act_scale_ptr = actp(l, SITE_DOWN); g.epi = FRT_EPI_NONE; g.partials = p_down; g.out = nullptr;
+      g.amax = nullptr;
       FRT_HIP(launch_gemm(g, s)); ++n;
 
       h_prev = h_mlp;
@@ -340,11 +404,38 @@ extern "C" int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_de
         (void)hipEventDestroy(ev);
       }
     }
+    // optional concurrent prefetch branch: a side stream and one fork event per layer-step
+    hipStream_t side = nullptr;
+    std::vector<hipEvent_t> evs;
+    hipEvent_t join = nullptr;
+    const int nls = desc->steps * desc->layers;
+    if (desc->prefetch_next) {
+      bool ok = hipStreamCreateWithFlags(&side, hipStreamNonBlocking) == hipSuccess &&
+                hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess;
+      evs.assign(nls, nullptr);
+      for (int i = 0; ok && i < nls; ++i) ok = hipEventCreateWithFlags(&evs[i], hipEventDisableTiming) == hipSuccess;
+      if (!ok) {
+        for (hipEvent_t ev : evs) if (ev) (void)hipEventDestroy(ev);
+        if (join) (void)hipEventDestroy(join);
+        if (side) (void)hipStreamDestroy(side);
+        (void)hipStreamDestroy(cs);
+        delete c;
+        return FRT_E_HIP;
+      }
+    }
     e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     int n = 0;
-    int rc = e == hipSuccess ? enqueue_chain(c, cs, &n) : FRT_E_HIP;
+    int rc = e == hipSuccess ? enqueue_chain(c, cs, &n, side, side ? evs.data() : nullptr) : FRT_E_HIP;
+    if (side && e == hipSuccess) {  // rejoin the side branch before the capture ends
+      hipError_t ej = hipEventRecord(join, side);
+      if (ej == hipSuccess) ej = hipStreamWaitEvent(cs, join, 0);
+      if (ej != hipSuccess && rc == FRT_OK) { set_hip_error((int)ej); rc = FRT_E_HIP; }
+    }
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(cs, &g);
+    for (hipEvent_t ev : evs) (void)hipEventDestroy(ev);
+    if (join) (void)hipEventDestroy(join);
+    if (side) (void)hipStreamDestroy(side);
     if (e != hipSuccess) set_hip_error((int)e);
     if (rc == FRT_OK && e2 != hipSuccess) { set_hip_error((int)e2); rc = FRT_E_HIP; }
     if (rc == FRT_OK) {
@@ -400,6 +491,28 @@ extern "C" int frt_layer_chain_run(frt_chain* c, void* stream) {
 }
 
 extern "C" int frt_layer_chain_kernel_count(const frt_chain* c) { return c ? c->kernels : -1; }
+
+__global__ void amax_to_scale_kernel(const unsigned* amax, float* scales, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) scales[i] = __builtin_bit_cast(float, amax[i]) / 448.0f;
+}
+
+extern "C" int frt_layer_chain_calibrate(frt_chain* c, void* stream, float* scales_dev) {
+  FRT_CHECK(c, FRT_E_STATE);
+  FRT_CHECK(c->d.dtype == FRT_BF16, FRT_E_DTYPE);
+  FRT_CHECK(scales_dev, FRT_E_NULL);
+  FRT_CHECK(aligned16(scales_dev), FRT_E_ALIGN);
+  const int n = c->d.layers * 4;
+  FRT_CHECK(!overlaps(scales_dev, (size_t)n * 4, c->arena, c->arena_bytes), FRT_E_ALIAS);
+  hipStream_t s = (hipStream_t)stream;
+  unsigned* amax = (unsigned*)at(c, c->L.amax);
+  FRT_HIP(hipMemsetAsync(amax, 0, (size_t)n * 4, s));
+  int rc = enqueue_chain(c, s, nullptr, nullptr, nullptr, amax);
+  if (rc != FRT_OK) return rc;
+  hipLaunchKernelGGL(amax_to_scale_kernel, dim3((n + 255) / 256), dim3(256), 0, s, (const unsigned*)amax, scales_dev, n);
+  FRT_HIP(hipGetLastError());
+  return FRT_OK;
+}
 
 extern "C" int frt_layer_chain_destroy(frt_chain* c) {
   FRT_CHECK(c, FRT_E_STATE);

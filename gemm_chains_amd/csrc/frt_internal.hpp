@@ -146,6 +146,14 @@ __device__ __forceinline__ void store_operand4(uint8_t* op, int dtype, int MB, i
 
 __device__ __forceinline__ float load_scale(const float* p, float v) { return p ? __ldg(p) : v; }
 
+// Calibration: fold |values| into a device-wide running maximum.  Non-negative floats
+// order like their bit patterns, so an unsigned atomic max is exact and order-free.
+__device__ __forceinline__ void record_amax(unsigned* amax, float a0, float a1, float a2, float a3) {
+  if (!amax) return;
+  const float m = fmaxf(fmaxf(fabsf(a0), fabsf(a1)), fmaxf(fabsf(a2), fabsf(a3)));
+  if (m > 0.f) atomicMax(amax, __builtin_bit_cast(unsigned, m));
+}
+
 // Four consecutive columns n0..n0+3 of row m of a fused QKV output, rounded to bf16 and
 // written where attention reads them (the section boundaries are multiples of 16):
 // Q row-major [m][nq], K row-major [m][hd], V transposed v_out[d * v_ld + m].
@@ -182,6 +190,7 @@ struct RnqParams {
   float act_scale;
   const float* act_scale_ptr;
   uint8_t* operand;          // packed or null
+  unsigned* amax;            // calibration: running max |value before rounding| (float bits), or null
 };
 
 struct GemmParams {
@@ -205,6 +214,7 @@ struct GemmParams {
   uint16_t* k_out;
   uint16_t* v_out;
   int nq, hd, v_ld;
+  unsigned* amax;            // calibration of the SiLU-gate output, or null
 };
 
 struct ReduceParams {
@@ -222,6 +232,7 @@ struct ReduceParams {
   uint16_t* k_out;
   uint16_t* v_out;
   int nq, hd, v_ld;
+  unsigned* amax;
 };
 
 struct AttnParams {
@@ -236,6 +247,7 @@ struct AttnParams {
   const float* out_scale_ptr;
   uint8_t* operand;
   float* workspace;          // chunk partial records when the key axis is split
+  unsigned* amax;            // calibration of the attention output, or null
 };
 
 // Epilogue codes used inside the library beyond the public frt_epilogue values.

@@ -195,6 +195,7 @@ __global__ void __launch_bounds__(512) skinny_gemm_kernel(const GemmParams p) {
     for (int r = 0; r < 4; ++r) z[r] = silu_f(cg[r]) * cu[r];
     store_operand4(reinterpret_cast<uint8_t*>(p.out), p.out_dtype, MB, m, ng, z[0], z[1], z[2], z[3], os,
                    m >= p.M);
+    if (m < p.M) record_amax(p.amax, z[0], z[1], z[2], z[3]);
   };
   const bool silu = !partial_out && p.epi == FRT_EPI_SILU_GATE_QUANT;
 
@@ -260,6 +261,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceParams p
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[r] = silu_f(cg[r]) * cu[r];
     store_operand4(reinterpret_cast<uint8_t*>(p.out), p.out_dtype, p.MB, m, n0, z[0], z[1], z[2], z[3], os, false);
+    record_amax(p.amax, z[0], z[1], z[2], z[3]);
     return;
   }
   const f32x4 c = reduce4(n0);

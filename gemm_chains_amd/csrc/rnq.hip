@@ -77,6 +77,7 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
     if (p.ada_scale) y = y * (1.0f + *reinterpret_cast<const f32x4*>(p.ada_scale + k0));
     if (p.ada_shift) y = y + *reinterpret_cast<const f32x4*>(p.ada_shift + k0);
     store_operand4(p.operand, p.out_dtype, p.MB, m, k0, y.x, y.y, y.z, y.w, as, false);
+    record_amax(p.amax, y.x, y.y, y.z, y.w);
   }
 }
 

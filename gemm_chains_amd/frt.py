@@ -35,7 +35,7 @@ class ChainDesc(ctypes.Structure):
     _fields_ = [("layers", _int), ("steps", _int), ("M", _int), ("hidden", _int), ("n_heads", _int),
                 ("head_dim", _int), ("prefix_len", _int), ("mlp", _int), ("dtype", _int), ("eps", _float),
                 ("splits_qkv", _int), ("splits_o", _int), ("splits_up", _int), ("splits_down", _int),
-                ("use_graph", _int), ("keep_intermediates", _int),
+                ("use_graph", _int), ("keep_intermediates", _int), ("prefetch_next", _int),
                 ("w_qkv", ctypes.POINTER(_c_void_p)), ("w_o", ctypes.POINTER(_c_void_p)),
                 ("w_up", ctypes.POINTER(_c_void_p)), ("w_down", ctypes.POINTER(_c_void_p)),
                 ("s_qkv", ctypes.POINTER(_c_void_p)), ("s_o", ctypes.POINTER(_c_void_p)),
@@ -72,6 +72,7 @@ _SIGS = {
     "frt_layer_chain_buffer": (_int, [_c_void_p, ctypes.c_char_p, ctypes.POINTER(_c_void_p),
                                       ctypes.POINTER(_size)]),
     "frt_layer_chain_run": (_int, [_c_void_p, _c_void_p]),
+    "frt_layer_chain_calibrate": (_int, [_c_void_p, _c_void_p, _c_void_p]),
     "frt_layer_chain_kernel_count": (_int, [_c_void_p]),
     "frt_layer_chain_destroy": (_int, [_c_void_p]),
 }
@@ -228,7 +229,7 @@ def _ptr_array(ptrs):
 
 def make_chain_desc(layers, steps, M, hidden, n_heads, head_dim, prefix_len, mlp, dtype, eps, splits,
                     w_qkv, w_o, w_up, w_down, s_qkv=None, s_o=None, s_up=None, s_down=None, use_graph=True,
-                    keep_intermediates=False):
+                    keep_intermediates=False, prefetch_next=False):
     """Build a ChainDesc; returns (desc, keepalive) -- keep both alive while the chain exists."""
     keep = []
     d = ChainDesc()
@@ -237,6 +238,7 @@ def make_chain_desc(layers, steps, M, hidden, n_heads, head_dim, prefix_len, mlp
     d.dtype, d.eps = dtype, eps
     d.splits_qkv, d.splits_o, d.splits_up, d.splits_down = splits
     d.use_graph, d.keep_intermediates = int(bool(use_graph)), int(bool(keep_intermediates))
+    d.prefetch_next = int(bool(prefetch_next))
     for name, ptrs in (("w_qkv", w_qkv), ("w_o", w_o), ("w_up", w_up), ("w_down", w_down),
                        ("s_qkv", s_qkv), ("s_o", s_o), ("s_up", s_up), ("s_down", s_down)):
         if ptrs is None:
@@ -269,6 +271,10 @@ def frt_layer_chain_buffer(chain, name):
 
 def frt_layer_chain_run(chain, stream=None):
     _check(_lib().frt_layer_chain_run(chain, _stream(stream)), "frt_layer_chain_run")
+
+
+def frt_layer_chain_calibrate(chain, scales, stream=None):
+    _check(_lib().frt_layer_chain_calibrate(chain, _stream(stream), _ptr(scales)), "frt_layer_chain_calibrate")
 
 
 def frt_layer_chain_kernel_count(chain):

@@ -231,6 +231,9 @@ typedef struct frt_chain_desc {
   int splits_qkv, splits_o, splits_up, splits_down;   /* 0 = library choice            */
   int use_graph;             /* 1: capture once, replay with one hipGraphLaunch          */
   int keep_intermediates;    /* 1: every (step, layer) writes its own debug buffers      */
+  int prefetch_next;         /* 1 (graph only): a concurrent branch reads the next layer's
+                                weights while the current layer runs, so its GEMMs find
+                                them in the last-level cache (the launch-overlap analogue) */
   /* host arrays of `layers` device pointers to packed weights (frt_pack_weight):
    * qkv [hidden][(n_heads+2)*head_dim] plain, o [n_heads*head_dim][hidden] plain,
    * up [hidden][2*mlp] FRT_W_GATE_UP, down [mlp][hidden] plain.                        */
@@ -271,6 +274,16 @@ int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_dev, size_t a
  *   [steps][layers][M][n_heads*head_dim] bf16; each (step, layer) slice starts on a
  *   256-byte boundary.  A name whose buffer is empty returns FRT_E_STATE.              */
 int frt_layer_chain_buffer(frt_chain* chain, const char* name, void** dev, size_t* bytes);
+/* Static activation scales for an e4m3 chain built from the same bf16 master weights:
+ * runs this bf16 chain once, eagerly, on the current "x_in" / "mod" / caches (the
+ * calibration inputs), records max |value| at every GEMM-input site (qkv, o, up, down of
+ * each layer, over every flow step) before its bf16 rounding, and writes
+ * scales_dev[l*4 + site] = max / 448 (fp32, device, [layers][4]).  The scales are then
+ * fixed for every later run (notes, section "静态量化改变了两次矩阵乘之间的工作": scales
+ * fixed ahead of the run, weight and activation scales kept apart).  Also writes
+ * "x_out" like a run.  FRT_E_DTYPE unless the chain is bf16.                          */
+int frt_layer_chain_calibrate(frt_chain* chain, void* stream, float* scales_dev);
+
 /* Run every step and layer once on `stream` (one hipGraphLaunch, or eager launches). */
 int frt_layer_chain_run(frt_chain* chain, void* stream);
 /* Kernels one run launches (graph nodes when captured). */

@@ -346,9 +346,10 @@ def chain(x0, weights, scales, k_prefix, v_prefix, mod, dims, dtype, eps,
 def calibrate(x0_cal, weights, k_prefix, v_prefix, mod_cal, dims, eps):
     """Static activation scales from one un-quantised run on calibration inputs.
 
-    For every layer and each of its 4 GEMM-input sites, s = fp32(max |y| / 448) over
-    every flow step ([notes] static-quantisation section: scales fixed ahead of the
-    run and reused; weight and activation scales kept apart).  Returns [L][4].
+    weights: the model's master weights (decoded bf16 values; reading R13).  For every
+    layer and each of its 4 GEMM-input sites, s = fp32(max |y| / 448) over every flow
+    step ([notes] static-quantisation section: scales fixed ahead of the run and reused;
+    weight and activation scales kept apart).  Returns [L][4].
     """
     rec = {}
     chain(x0_cal, weights, np.ones((len(weights), 4)), k_prefix, v_prefix, mod_cal, dims,

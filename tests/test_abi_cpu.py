@@ -232,6 +232,7 @@ def test_chain_validation():
     assert lib.frt_layer_chain_create(ctypes.byref(d), FAKE, n, None, ctypes.byref(h)) == frt.E_SPLITK
     assert lib.frt_layer_chain_buffer(None, b"x_in", None, None) == frt.E_STATE
     assert lib.frt_layer_chain_run(None, None) == frt.E_STATE
+    assert lib.frt_layer_chain_calibrate(None, None, None) == frt.E_STATE
     assert lib.frt_layer_chain_destroy(None) == frt.E_STATE
     assert lib.frt_layer_chain_kernel_count(None) == -1
     # keep_intermediates grows the arena by the per-(step, layer) debug buffers
