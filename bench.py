@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+COPY_BYTES = 256 << 20  # the reference streaming kernel of the traffic counter passes
 
 
 def log(msg):
@@ -100,6 +101,28 @@ def time_dominant_gemm(torch, frt, device, synth, dims, dtype, reps=128):
     return us, wbytes + extra, splits
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gate_up_gemm_bf16_m50_hbm_traffic.md")
+GEMM_SOURCES = [os.path.join(ROOT, "gemm_chains_amd", "csrc", f) for f in ("gemm.hip", "frt_internal.hpp")]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a streaming kernel of known size), or None when the
+    kernel's sources changed since the counters were taken (hash recorded in the summary)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE, encoding="utf-8").read()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines() if l.startswith(("source_sha256:", "traffic_bytes_")))
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    if fields.get("source_sha256", "").strip() != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_launch"].strip())
+
+
 def cpu_baseline(synth, dims_full, budget_s=12.0):
     """The float64 oracle on a bounded sample of the same workload: all 18 layers of the
     first flow steps, as many steps as fit the budget (at least one)."""
@@ -139,6 +162,9 @@ def main():
     ap.add_argument("--layers", type=int, default=18)
     ap.add_argument("--flow-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dominant-only", action="store_true",
+                    help="run only the dominant GEMM's timed graph and a plain copy of known size "
+                         "(the program the HBM-traffic counter passes profile)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the single-batch action-decoder chain is a "
@@ -151,6 +177,19 @@ def main():
     from gemm_chains_amd import chain, device, frt
     frt.lib()
     torch.cuda.set_device(0)
+
+    if args.dominant_only:
+        dims = synth.chain_dims(layers=1, steps=1, M=50)
+        us, nbytes, splits = time_dominant_gemm(torch, frt, device, synth, dims, frt.BF16)
+        # a plain streaming kernel of known size: the scale of the HBM byte counters
+        src_t = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        for _ in range(4):
+            torch.neg(src_t, out=dst_t)
+        torch.cuda.synchronize()
+        print(json.dumps({"dominant_us_per_launch": round(us, 3), "bytes": nbytes, "splits": splits,
+                          "copy_bytes_each_way": COPY_BYTES}), flush=True)
+        return
 
     results = {}
     for M in (50, 10):
@@ -237,7 +276,7 @@ def main():
         "weight_stream_gbs": round(r["weight_gbs"], 1),
         "weight_stream_frac_of_peak": round(r["weight_gbs"] / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": f"skinny_gemm gate|up {dims50['M']}x{dims50['hidden']}x{2 * dims50['mlp']} "
                                f"bf16 s={splits} +SiLU epilogue", "us_per_launch": round(us, 3)},
         "cpu_baseline": cpu,
