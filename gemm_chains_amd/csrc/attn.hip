@@ -253,7 +253,10 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
 }
 
 // Merge of the chunk records: workgroup = (head h, 16-row block mb); thread -> (query row,
-// 8 d); chunks in order (deterministic).
+// 8 d); chunks in order (deterministic).  With CH > 0 (nch <= CH) every record of the
+// thread is loaded before the first is used, so the records, written by the previous
+// kernel on other XCDs, cost one memory latency instead of one per chunk.
+template <int CH>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, int nch) {
   const int h = blockIdx.x, mb = blockIdx.y, MB = gridDim.y;
   const int tq = threadIdx.x >> 4;
@@ -261,20 +264,41 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
   const float NEG_INF = -__builtin_huge_valf();
   const float* rec0 = p.workspace + ((size_t)h * MB + mb) * attn_record_floats();
   const size_t cstride = (size_t)p.n_heads * MB * attn_record_floats();
-  float mx = NEG_INF;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, rec0[c * cstride + tq]);
-  float den = 0.f, num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < nch; ++c) {
-    const float* rc = rec0 + c * cstride;
-    const float mc = rc[tq];
+  float mx = NEG_INF, den = 0.f, num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](float mc, float lc, f32x4 a, f32x4 b) {
     const float wc = mc == NEG_INF ? 0.f : expf(mc - mx);
-    den += wc * rc[16 + tq];
-    const f32x4 a = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0 + 4);
+    den += wc * lc;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       num[e] += wc * a[e];
       num[4 + e] += wc * b[e];
+    }
+  };
+  if constexpr (CH > 0) {
+    float mc[CH], lc[CH];
+    f32x4 a[CH], b[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c < nch) {
+        const float* rc = rec0 + c * cstride;
+        mc[c] = rc[tq];
+        lc[c] = rc[16 + tq];
+        a[c] = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0);
+        b[c] = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0 + 4);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (c < nch) mx = fmaxf(mx, mc[c]);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (c < nch) add(mc[c], lc[c], a[c], b[c]);
+  } else {
+    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, rec0[c * cstride + tq]);
+    for (int c = 0; c < nch; ++c) {
+      const float* rc = rec0 + c * cstride;
+      add(rc[tq], rc[16 + tq], *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0),
+          *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0 + 4));
     }
   }
   const float os = load_scale(p.out_scale_ptr, p.out_scale);
@@ -302,7 +326,10 @@ hipError_t launch_attention(const AttnParams& p_in, hipStream_t s) {
     hipLaunchKernelGGL((attn_chunk_kernel<8, true>), dim3(p.n_heads, p.MB, nch), dim3(512), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nch == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(p.n_heads, p.MB), dim3(256), 0, s, p, nch);
+  const dim3 g(p.n_heads, p.MB), b(256);
+  if (nch <= 8) hipLaunchKernelGGL(attn_combine_kernel<8>, g, b, 0, s, p, nch);
+  else if (nch <= 16) hipLaunchKernelGGL(attn_combine_kernel<16>, g, b, 0, s, p, nch);
+  else hipLaunchKernelGGL(attn_combine_kernel<0>, g, b, 0, s, p, nch);
   return hipGetLastError();
 }
 

@@ -127,6 +127,39 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 }
 __device__ __forceinline__ uint32_t bf16_pack2(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
 
+// Single rounding of a float64 value whose float32 rounding may land exactly on a
+// rounding boundary of the narrow format although the float64 value does not (double
+// rounding): in that case step the float32 value one ulp towards the float64 one, so the
+// narrow format's round-to-nearest-even sees the side the exact value is on.
+__device__ __forceinline__ float toward(float f, double exact) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const bool away = (double)f < exact ? f >= 0.f : f <= 0.f;  // magnitude grows
+  return __builtin_bit_cast(float, away ? u + 1u : u - 1u);
+}
+// bf16 code of a float64 value, rounded once (weights folded with gamma).
+__device__ __forceinline__ uint32_t bf16_bits_exact(double x) {
+  float f = (float)x;
+  if ((__builtin_bit_cast(uint32_t, f) & 0xffffu) == 0x8000u && (double)f != x) f = toward(f, x);
+  return bf16_bits(f);
+}
+// E4M3 code of a float64 value, rounded once: boundaries sit at 4 bits of significand in
+// the normal range (|v| >= 2^-6) and at odd multiples of 2^-10 below it.
+__device__ __forceinline__ uint32_t e4m3_code_exact(double x) {
+  float f = (float)x;
+  const float a = fabsf(f);
+  if ((double)f != x && a < 448.0f) {
+    bool mid;
+    if (a >= 0.015625f) {
+      mid = (__builtin_bit_cast(uint32_t, a) & 0xfffffu) == 0x80000u;
+    } else {
+      const float t = a * 512.0f;  // exact
+      mid = t - floorf(t) == 0.5f;
+    }
+    if (mid) f = toward(f, x);
+  }
+  return e4m3_code(f);
+}
+
 // Write 4 consecutive logical k (k % 4 == 0) of row m of a packed operand.
 // e4m3 values are divided by the static activation scale first (correctly rounded).
 __device__ __forceinline__ void store_operand4(uint8_t* op, int dtype, int MB, int m, int k, float v0,

@@ -231,7 +231,9 @@ __global__ void __launch_bounds__(512) skinny_gemm_kernel(const GemmParams p) {
 
 // Consumer: fixed-order split-K reduction + scale recovery + epilogue.  One thread per
 // 4 consecutive columns of one row (rows up to Mp for the SiLU epilogue, whose padding
-// rows are written as zero codes).
+// rows are written as zero codes).  SPL >= splits is a compile-time bound so that every
+// slice's load is issued before the sum starts (one memory latency, not one per slice).
+template <int SPL>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceParams p) {
   const float as = load_scale(p.act_scale_ptr, p.act_scale);
   const int ncols = p.epi == FRT_EPI_SILU_GATE_QUANT ? p.N / 2 : p.N;
@@ -244,8 +246,14 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceParams p
   const size_t sstride = (size_t)p.M * p.N;
   auto reduce4 = [&](int n) {
     const float* src = p.partials + (size_t)m * p.N + n;
-    f32x4 v = *reinterpret_cast<const f32x4*>(src);
-    for (int j = 1; j < p.splits; ++j) v += *reinterpret_cast<const f32x4*>(src + j * sstride);
+    f32x4 pj[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j)
+      if (j < p.splits) pj[j] = *reinterpret_cast<const f32x4*>(src + j * sstride);
+    f32x4 v = pj[0];
+#pragma unroll
+    for (int j = 1; j < SPL; ++j)
+      if (j < p.splits) v += pj[j];
     v *= as;
     if (p.colscale) v *= *reinterpret_cast<const f32x4*>(p.colscale + n);
     return v;
@@ -339,7 +347,11 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
   const int ncols = p.epi == FRT_EPI_SILU_GATE_QUANT ? p.N / 2 : p.N;
   const int rows = p.epi == FRT_EPI_SILU_GATE_QUANT ? p.MB * 16 : p.M;
   const int total = rows * (ncols / 4);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, s, p);
+  const dim3 g((total + 255) / 256), b(256);
+  if (p.splits <= 2) hipLaunchKernelGGL(splitk_reduce_kernel<2>, g, b, 0, s, p);
+  else if (p.splits <= 4) hipLaunchKernelGGL(splitk_reduce_kernel<4>, g, b, 0, s, p);
+  else if (p.splits <= 8) hipLaunchKernelGGL(splitk_reduce_kernel<8>, g, b, 0, s, p);
+  else hipLaunchKernelGGL(splitk_reduce_kernel<16>, g, b, 0, s, p);
   return hipGetLastError();
 }
 

@@ -12,19 +12,20 @@
 
 namespace frt {
 
-// s_w[n] = max_k |gamma[k] * W[k][n]| / 448 (fp32), one thread per column; consecutive
-// threads read consecutive columns of a row, so every row read is coalesced.
+// s_w[n] = max_k |gamma[k] * W[k][n]| / 448, one thread per column; consecutive threads
+// read consecutive columns of a row, so every row read is coalesced.  The products are
+// exact in float64 (8 x 24 significand bits) and the quotient is rounded once to fp32.
 __global__ void __launch_bounds__(256) colscale_kernel(const uint16_t* __restrict__ w, const float* __restrict__ gamma,
                                                        int K, int N, float* __restrict__ colscale) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
-  float amax = 0.f;
+  double amax = 0.0;
   for (int k = 0; k < K; ++k) {
-    float v = bf16_to_f32(w[(size_t)k * N + n]);
-    if (gamma) v *= gamma[k];
-    amax = fmaxf(amax, fabsf(v));
+    double v = (double)bf16_to_f32(w[(size_t)k * N + n]);
+    if (gamma) v *= (double)gamma[k];
+    amax = fmax(amax, fabs(v));
   }
-  colscale[n] = amax / 448.0f;
+  colscale[n] = (float)(amax / 448.0);
 }
 
 // One thread per 16-byte lane slot of the packed weight.
@@ -51,29 +52,31 @@ __global__ void __launch_bounds__(256) pack_weight_kernel(const uint16_t* __rest
   const int k0 = ks * KSTEP + (lane >> 4) * (KSTEP / 4) + half * 16;
   u32x4 v;
   uint32_t* vw = reinterpret_cast<uint32_t*>(&v);
+  // W' = gamma * W and W' / s_w are formed in float64 (the product is exact, the quotient
+  // correctly rounded) and rounded once to the storage format
   if (dtype == FRT_BF16) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      float a = bf16_to_f32(w[(size_t)(k0 + e) * N + n]);
-      float b = bf16_to_f32(w[(size_t)(k0 + e + 1) * N + n]);
+      double a = (double)bf16_to_f32(w[(size_t)(k0 + e) * N + n]);
+      double b = (double)bf16_to_f32(w[(size_t)(k0 + e + 1) * N + n]);
       if (gamma) {
-        a *= gamma[k0 + e];
-        b *= gamma[k0 + e + 1];
+        a *= (double)gamma[k0 + e];
+        b *= (double)gamma[k0 + e + 1];
       }
-      vw[e / 2] = bf16_pack2(a, b);
+      vw[e / 2] = bf16_bits_exact(a) | (bf16_bits_exact(b) << 16);
     }
   } else {
-    const float s = colscale[n];
+    const double s = (double)colscale[n];
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
-      float x[4];
+      uint32_t word = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float a = bf16_to_f32(w[(size_t)(k0 + e + q) * N + n]);
-        if (gamma) a *= gamma[k0 + e + q];
-        x[q] = s > 0.f ? a / s : 0.f;
+        double a = (double)bf16_to_f32(w[(size_t)(k0 + e + q) * N + n]);
+        if (gamma) a *= (double)gamma[k0 + e + q];
+        word |= (s > 0.0 ? e4m3_code_exact(a / s) : 0u) << (8 * q);
       }
-      vw[e / 4] = e4m3_pack4(x[0], x[1], x[2], x[3]);
+      vw[e / 4] = word;
     }
   }
   *reinterpret_cast<u32x4*>(out + slot * 16) = v;

@@ -22,6 +22,11 @@ namespace frt {
 
 constexpr int kRnqGroups = kMaxProducerK / 1024;  // 4-element groups per thread, max
 
+// SPL = number of fp32 partial slices read (0: no x; otherwise a power of two >= x_splits,
+// slices past x_splits are skipped by a uniform predicate).  Every load of a group is
+// issued before the first one is used: the partials come from the previous kernel and
+// sit beyond this XCD's L2, so a serial chain of loads would pay that latency per slice.
+template <int SPL>
 __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
@@ -48,18 +53,33 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
     if (k0 >= K) break;
     const f32x4 r = *reinterpret_cast<const f32x4*>(p.residual + row + k0);
     f32x4 hv = r;
-    if (p.x) {
-      f32x4 x = *reinterpret_cast<const f32x4*>(p.x + row + k0);
-      for (int j = 1; j < p.x_splits; ++j) x += *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
-      x *= xs;  // partials summed in ascending split order, then scale recovery
-      if (p.x_colscale) x *= *reinterpret_cast<const f32x4*>(p.x_colscale + k0);
-      if (p.gate) x *= *reinterpret_cast<const f32x4*>(p.gate + k0);
+    if constexpr (SPL > 0) {
+      f32x4 xp[SPL];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j)
+        if (j < p.x_splits) xp[j] = *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
+      const f32x4 cs = p.x_colscale ? *reinterpret_cast<const f32x4*>(p.x_colscale + k0) : f32x4{1.f, 1.f, 1.f, 1.f};
+      const f32x4 gt = p.gate ? *reinterpret_cast<const f32x4*>(p.gate + k0) : f32x4{1.f, 1.f, 1.f, 1.f};
+      f32x4 x = xp[0];
+#pragma unroll
+      for (int j = 1; j < SPL; ++j)
+        if (j < p.x_splits) x += xp[j];  // partials summed in ascending split order
+      x *= xs;                           // then scale recovery
+      if (p.x_colscale) x *= cs;
+      if (p.gate) x *= gt;
       hv = r + x;
     }
-    if (p.residual_out) *reinterpret_cast<f32x4*>(p.residual_out + row + k0) = hv;
     h[i] = hv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ss = fmaf(hv[e], hv[e], ss);
+  }
+  if (p.residual_out) {
+#pragma unroll
+    for (int i = 0; i < kRnqGroups; ++i) {
+      const int k0 = 4 * (tid + 256 * i);
+      if (k0 >= K) break;
+      *reinterpret_cast<f32x4*>(p.residual_out + row + k0) = h[i];
+    }
   }
   if (!p.operand) return;
 #pragma unroll
@@ -83,7 +103,14 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
 
 hipError_t launch_rnq(const RnqParams& p, hipStream_t s) {
   const int rows = p.operand ? p.MB * 16 : p.M;
-  hipLaunchKernelGGL(rnq_kernel, dim3(rows), dim3(256), 0, s, p);
+  const dim3 g(rows), b(256);
+  const int sp = p.x ? p.x_splits : 0;
+  if (sp == 0) hipLaunchKernelGGL(rnq_kernel<0>, g, b, 0, s, p);
+  else if (sp == 1) hipLaunchKernelGGL(rnq_kernel<1>, g, b, 0, s, p);
+  else if (sp == 2) hipLaunchKernelGGL(rnq_kernel<2>, g, b, 0, s, p);
+  else if (sp <= 4) hipLaunchKernelGGL(rnq_kernel<4>, g, b, 0, s, p);
+  else if (sp <= 8) hipLaunchKernelGGL(rnq_kernel<8>, g, b, 0, s, p);
+  else hipLaunchKernelGGL(rnq_kernel<16>, g, b, 0, s, p);
   return hipGetLastError();
 }
 

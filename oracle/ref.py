@@ -360,3 +360,19 @@ def calibrate(x0_cal, weights, k_prefix, v_prefix, mod_cal, dims, eps):
         for s, m in sites.items():
             amax[l, s] = max(amax[l, s], m)
     return f32(amax / codec.E4M3_MAX)
+
+
+def calibrate_block(residual, x, gate, ada_scale, ada_shift, w_up, eps):
+    """Static scales of a lone producer -> gate|up GEMM -> SiLU-gate block (the FP8
+    single-layer and GEMM-sweep workloads) from one un-quantised run on calibration inputs.
+
+    w_up: master weights (decoded bf16 values, [K][2F], gate | up columns; reading R13).
+    Site 0 is the producer's output y = AdaRMSNorm(r + gate * x), site 1 the SiLU-gate
+    output z = SiLU(y W_gate) * (y W_up) that feeds the down projection; each scale is
+    fp32(max |value| / 448) ([notes] static-quantisation section).  Returns (s_y, s_z).
+    """
+    o = residual_norm_quant(residual, None if x is None else _f64(x)[None], None, 1.0, gate,
+                            ada_scale, ada_shift, eps, "bf16", 1.0)
+    z = silu_gate(o["y"] @ _f64(w_up))
+    return (float(f32(np.max(np.abs(o["y"])) / codec.E4M3_MAX)),
+            float(f32(np.max(np.abs(z)) / codec.E4M3_MAX)))

@@ -60,3 +60,14 @@ def rel_l2(a, b):
 
 def bf16_values(bits):
     return codec.bf16_decode(np.asarray(bits).view(np.uint16))
+
+
+def silu_gate_mag(c, a_dec, w_dec, act, s_w, dtype, out_scale):
+    """Summand sizes of z = SiLU(gate) * up for the tie band: the GEMM sums feeding gate
+    and up (|SiLU'| <= 1.1) and the product itself, scaled like the rounded value."""
+    from oracle import ref
+    g_mag = (np.abs(a_dec) @ np.abs(w_dec)) * act * (np.asarray(s_w)[None, :] if s_w is not None else 1.0)
+    n2 = c.shape[1] // 2
+    gte, up = c[:, :n2], c[:, n2:]
+    mag = 1.1 * np.abs(up) * g_mag[:, :n2] + np.abs(ref.silu(gte)) * g_mag[:, n2:] + np.abs(ref.silu(gte) * up)
+    return mag / out_scale if dtype == "e4m3" else mag

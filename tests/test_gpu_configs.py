@@ -1,0 +1,278 @@
+"""GPU parity of the four stand-alone workloads, composed the way each is described, against
+the oracle (MI355X only).
+
+  1  fused residual + RMSNorm + bf16 GEMM, M=10, K=N=1024, gamma folded into W, s in {1,2,4}
+  2  gated MLP at M=50: up (1024 -> 8192 gate|up) + SiLU gate, then down (4096 -> 1024),
+     s in {1,2,4,8} per GEMM
+  3  FP8 static-scale block at M=10: gated residual + AdaRMSNorm -> e4m3, fused QKV
+     (1024 -> 2560), gate|up (1024 -> 8192) + SiLU gate -> e4m3, down (4096 -> 1024)
+  5  gate|up GEMM sweep, K=2048, N=16384, M in {1,10,16,32,50,64}, bf16 and e4m3,
+     split-K from the library's table
+
+Every GPU step runs on the GPU's own upstream outputs; the oracle runs its own pipeline on
+the same seeded inputs (it never reads a GPU output).  Bars:
+  - operand codes: the tie band (tests/helpers.py); packed weights: bit-exact;
+  - GEMM outputs (the reduced, scale-recovered fp32 C): relative L2 <= 5e-3 (bf16) and
+    <= 2e-3 (e4m3) against the oracle's quantisation-emulating path; split-K against
+    unsplit on the GPU <= 1e-5 (bf16) / 1e-4 (e4m3);
+  - codes that a GEMM epilogue rounds (the SiLU-gate output) are checked teacher-forced:
+    the GPU GEMM is fed the oracle's operand codes (host-packed) and its codes must match
+    up to the tie band; end to end (on the GPU's own operand) their decoded values must
+    stay within the GEMM-output bar.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import codec, ref
+from tests.helpers import check_codes, rel_l2, silu_gate_mag
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X GPU")
+    from gemm_chains_amd import frt, device
+    frt.lib()  # raises if the HIP library is missing
+    return frt, device
+
+
+def _silu_teacher_forced(frt, dev, M, N, K, s, dt, dtype, o, w_pk, cs, w_dec, s_w, act, out_act, label):
+    """SiLU-gate epilogue on the oracle's operand codes: codes up to the tie band."""
+    a_pk = dev.to_dev(frt.frt_operand_pack_host(o["codes"], dt, M, K))
+    c = ref.reduce_partials(ref.gemm_splitk(o["deq"], w_dec, 1), act, s_w)
+    z = ref.silu_gate_quant(c, dtype, out_act)
+    out = _silu(frt, dev, M, N, K, s, dt, a_pk, w_pk, cs, act, out_act)
+    torch.cuda.synchronize()
+    zc = dev.operand_codes(out, dt, _mp(M), N // 2)
+    check_codes(zc[:M], z["v"], silu_gate_mag(c, o["deq"], w_dec, act, s_w, dtype, out_act), dtype, label=label)
+    assert np.all(zc[M:] == 0)
+    return z
+
+
+def _producer(frt, dev, M, K, r, x, gate, sc, sh, eps, dt, act):
+    T = dev.to_dev
+    op = dev.empty_bytes(frt.frt_operand_bytes(dt, M, K))
+    h = dev.empty_f32(M, K)
+    frt.frt_residual_norm_quant(M, K, T(x[None]), 1, 1.0, None, T(r), h, None if gate is None else T(gate),
+                                None if sc is None else T(sc), None if sh is None else T(sh), eps, dt, act, op)
+    return op
+
+
+def _gemm_f32(frt, dev, M, N, K, s, dt, layout, a, w, cs, act):
+    parts = dev.empty_f32(s, M, N)
+    c = dev.empty_f32(M, N)
+    frt.frt_skinny_gemm_splitk(M, N, K, s, dt, layout, a, w, cs, act, parts, parts.numel() * 4,
+                               frt.EPI_STORE_F32, c, frt.F32, 1.0)
+    return c
+
+
+def _silu(frt, dev, M, N, K, s, dt, a, w, cs, act, out_act):
+    out = dev.empty_bytes(frt.frt_operand_bytes(dt, M, N // 2))
+    out.fill_(0xCD)
+    parts = dev.empty_f32(s, M, N) if s != 1 else None
+    frt.frt_skinny_gemm_splitk(M, N, K, s, dt, frt.W_GATE_UP, a, w, cs, act, parts,
+                               0 if parts is None else parts.numel() * 4, frt.EPI_SILU_GATE_QUANT, out, dt, out_act)
+    return out
+
+
+def _mp(M):
+    return 16 * math.ceil(M / 16)
+
+
+# ------------------------------------------------------------------ workload 1
+
+def test_config1_fused_rmsnorm_bf16_gemm(F):
+    frt, dev = F
+    w1 = synth.workload1()
+    M, K, N, eps = w1["M"], w1["K"], w1["N"], w1["eps"]
+    wp, _ = dev.pack_weight(w1["w"], frt.BF16, frt.W_PLAIN, gamma=w1["gamma"])
+    op = _producer(frt, dev, M, K, w1["r"], w1["x"], None, None, None, eps, frt.BF16, 1.0)
+    torch.cuda.synchronize()
+    # oracle: producer codes, W' = bf16(diag(gamma) W), and the emulating GEMM
+    o = ref.residual_norm_quant(w1["r"], w1["x"][None], None, 1.0, None, None, None, eps, "bf16")
+    wcodes, _, _ = ref.pack_weight_values(codec.bf16_decode(w1["w"]), w1["gamma"], "bf16")
+    check_codes(dev.operand_codes(op, frt.BF16, _mp(M), K)[:M], o["v"], o["mag"], "bf16", label="config 1 operand")
+    assert np.array_equal(dev.weight_codes(wp, frt.BF16, K, N), wcodes), "W' = bf16(diag(gamma) W), rounded once"
+    c_emul = ref.reduce_partials(ref.gemm_splitk(o["deq"], codec.bf16_decode(wcodes), 1))
+    # the plain definition y = (xhat * gamma) W that the fused path reaches
+    c_plain = ref.rmsnorm_matmul(ref.gated_residual(w1["r"], None, w1["x"]), w1["gamma"],
+                                 codec.bf16_decode(w1["w"]), eps)
+    outs = {}
+    for s in (1, 2, 4):
+        c = _gemm_f32(frt, dev, M, N, K, s, frt.BF16, frt.W_PLAIN, op, wp, None, 1.0)
+        cb = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        parts = dev.empty_f32(s, M, N)
+        frt.frt_skinny_gemm_splitk(M, N, K, s, frt.BF16, frt.W_PLAIN, op, wp, None, 1.0, parts, parts.numel() * 4,
+                                   frt.EPI_STORE_BF16, cb, frt.BF16, 1.0)
+        torch.cuda.synchronize()
+        outs[s] = dev.to_np(c)
+        assert rel_l2(outs[s], c_emul) <= 5e-3, f"s={s} vs emulating path"
+        assert rel_l2(outs[s], c_plain) <= 5e-3, f"s={s} vs plain definition"
+        bf = codec.bf16_decode(cb.cpu().numpy().view(np.uint16))
+        assert rel_l2(bf, c_emul) <= 5e-3, f"s={s} bf16 output"
+        print(f"config 1 s={s}: rel L2 vs emulating {rel_l2(outs[s], c_emul):.2e}, vs plain "
+              f"{rel_l2(outs[s], c_plain):.2e}")
+    for s in (2, 4):
+        assert rel_l2(outs[s], outs[1]) <= 1e-5, f"split {s} vs unsplit"
+
+
+# ------------------------------------------------------------------ workload 2
+
+def test_config2_gated_mlp_bf16(F):
+    frt, dev = F
+    w2 = synth.workload2()
+    M, K, Fm, eps = w2["M"], w2["K"], w2["mlp"], w2["eps"]
+    N_up = 2 * Fm
+    wu, _ = dev.pack_weight(w2["w_up"], frt.BF16, frt.W_GATE_UP)
+    wd, _ = dev.pack_weight(w2["w_down"], frt.BF16, frt.W_PLAIN)
+    op = _producer(frt, dev, M, K, w2["r"], w2["x"], None, None, None, eps, frt.BF16, 1.0)
+    o = ref.residual_norm_quant(w2["r"], w2["x"][None], None, 1.0, None, None, None, eps, "bf16")
+    wu_v, wd_v = codec.bf16_decode(w2["w_up"]), codec.bf16_decode(w2["w_down"])
+    c_up = ref.reduce_partials(ref.gemm_splitk(o["deq"], wu_v, 1))
+    z = ref.silu_gate_quant(c_up, "bf16")
+    c_down = ref.reduce_partials(ref.gemm_splitk(z["deq"], wd_v, 1))
+    torch.cuda.synchronize()
+    check_codes(dev.operand_codes(op, frt.BF16, _mp(M), K)[:M], o["v"], o["mag"], "bf16", label="config 2 operand")
+    zs = {}
+    for s in (1, 2, 4, 8):
+        _silu_teacher_forced(frt, dev, M, N_up, K, s, frt.BF16, "bf16", o, wu, None, wu_v, None, 1.0, 1.0,
+                             f"config 2 SiLU s={s}")
+        out = _silu(frt, dev, M, N_up, K, s, frt.BF16, op, wu, None, 1.0, 1.0)
+        torch.cuda.synchronize()
+        zc = dev.operand_codes(out, frt.BF16, _mp(M), Fm)
+        assert np.all(zc[M:] == 0)
+        zs[s] = out
+        e2e = rel_l2(codec.bf16_decode(zc[:M]), z["deq"])
+        assert e2e <= 5e-3, f"config 2 SiLU s={s} end to end"
+        print(f"config 2 up s={s}: SiLU output rel L2 end to end {e2e:.2e}")
+    downs = {}
+    for s in (1, 2, 4, 8):
+        c = _gemm_f32(frt, dev, M, K, Fm, s, frt.BF16, frt.W_PLAIN, zs[1], wd, None, 1.0)
+        torch.cuda.synchronize()
+        downs[s] = dev.to_np(c)
+        assert rel_l2(downs[s], c_down) <= 5e-3, f"down s={s}"
+        print(f"config 2 down s={s}: rel L2 {rel_l2(downs[s], c_down):.2e}")
+    for s in (2, 4, 8):
+        assert rel_l2(downs[s], downs[1]) <= 1e-5, f"down split {s} vs unsplit"
+    # teacher-forced down projection: the oracle's SiLU codes, host-packed
+    a_pk = dev.to_dev(frt.frt_operand_pack_host(z["codes"], frt.BF16, M, Fm))
+    c = _gemm_f32(frt, dev, M, K, Fm, 8, frt.BF16, frt.W_PLAIN, a_pk, wd, None, 1.0)
+    torch.cuda.synchronize()
+    assert rel_l2(dev.to_np(c), c_down) <= 1e-5
+
+
+# ------------------------------------------------------------------ workload 3
+
+def test_config3_fp8_static_scale_block(F):
+    frt, dev = F
+    w3 = synth.workload3()
+    cal = synth.workload3(seed=synth.CAL_SEED)
+    M, K, Fm, NQ, eps = w3["M"], w3["K"], w3["mlp"], w3["n_qkv"], w3["eps"]
+    sc, sh, gt = w3["mod"][0], w3["mod"][1], w3["mod"][2]
+    wq_v, wu_v, wd_v = (codec.bf16_decode(w3[n]) for n in ("w_qkv", "w_up", "w_down"))
+    # static activation scales from the calibration inputs (seed 1), on the master weights
+    s_y, s_z = ref.calibrate_block(cal["r"], cal["x"], cal["mod"][2], cal["mod"][0], cal["mod"][1], wu_v, eps)
+    E = frt.E4M3
+    wq, cq = dev.pack_weight(w3["w_qkv"], E, frt.W_PLAIN)
+    wu, cu = dev.pack_weight(w3["w_up"], E, frt.W_GATE_UP)
+    wd, cd = dev.pack_weight(w3["w_down"], E, frt.W_PLAIN)
+    op = _producer(frt, dev, M, K, w3["r"], w3["x"], gt, sc, sh, eps, E, s_y)
+    # oracle pipeline
+    o = ref.residual_norm_quant(w3["r"], w3["x"][None], None, 1.0, gt, sc, sh, eps, "e4m3", s_y)
+    qc, qs, _ = ref.pack_weight_values(wq_v, None, "e4m3")
+    uc, us, _ = ref.pack_weight_values(wu_v, None, "e4m3")
+    dc, ds, _ = ref.pack_weight_values(wd_v, None, "e4m3")
+    dec = codec.e4m3_decode
+    c_qkv = ref.reduce_partials(ref.gemm_splitk(o["deq"], dec(qc), 1), s_y, qs)
+    c_up = ref.reduce_partials(ref.gemm_splitk(o["deq"], dec(uc), 1), s_y, us)
+    z = ref.silu_gate_quant(c_up, "e4m3", s_z)
+    c_down = ref.reduce_partials(ref.gemm_splitk(z["deq"], dec(dc), 1), s_z, ds)
+    torch.cuda.synchronize()
+    check_codes(dev.operand_codes(op, E, _mp(M), K)[:M], o["v"], o["mag"], "e4m3", label="config 3 operand")
+    assert np.array_equal(dev.to_np(cq).astype(np.float64), qs)
+    assert np.array_equal(dev.to_np(cu).astype(np.float64), us)
+    qkv = {}
+    for s in (1, 2, 4, 8):
+        c = _gemm_f32(frt, dev, M, NQ, K, s, E, frt.W_PLAIN, op, wq, cq, s_y)
+        torch.cuda.synchronize()
+        qkv[s] = dev.to_np(c)
+        assert rel_l2(qkv[s], c_qkv) <= 2e-3, f"qkv s={s}"
+        print(f"config 3 qkv s={s}: rel L2 {rel_l2(qkv[s], c_qkv):.2e}")
+    for s in (2, 4, 8):
+        assert rel_l2(qkv[s], qkv[1]) <= 1e-4
+    _silu_teacher_forced(frt, dev, M, 2 * Fm, K, 1, E, "e4m3", o, wu, cu, dec(uc), us, s_y, s_z, "config 3 SiLU")
+    zo = _silu(frt, dev, M, 2 * Fm, K, 1, E, op, wu, cu, s_y, s_z)
+    torch.cuda.synchronize()
+    zc = dev.operand_codes(zo, E, _mp(M), Fm)
+    assert np.all(zc[M:] == 0)
+    c = _gemm_f32(frt, dev, M, K, Fm, 4, E, frt.W_PLAIN, zo, wd, cd, s_z)
+    torch.cuda.synchronize()
+    # End to end, a tie-band difference in one e4m3 operand code moves a whole column of
+    # the next GEMM, so downstream e4m3 codes can flip by a step (1/16 of a value).  The bar
+    # is the oracle's own sensitivity (as for the chain): perturb the producer's values by
+    # the tie-band width (2^-17 relative) before rounding, rerun the oracle, and allow twice
+    # the change that causes.
+    g = np.random.default_rng(3)
+    vp = o["v"] * (1.0 + 2.0 ** -17 * g.standard_normal(o["v"].shape))
+    a_p = codec.e4m3_decode(codec.e4m3_encode(vp))
+    z_p = ref.silu_gate_quant(ref.reduce_partials(ref.gemm_splitk(a_p, dec(uc), 1), s_y, us), "e4m3", s_z)
+    c_down_p = ref.reduce_partials(ref.gemm_splitk(z_p["deq"], dec(dc), 1), s_z, ds)
+    sens_z, sens_d = rel_l2(z_p["deq"], z["deq"]), rel_l2(c_down_p, c_down)
+    e2e_z, e2e = rel_l2(dec(zc[:M]), z["deq"]), rel_l2(dev.to_np(c), c_down)
+    print(f"config 3 end to end: SiLU output rel L2 {e2e_z:.2e} (oracle sensitivity {sens_z:.2e}), "
+          f"down rel L2 {e2e:.2e} (sensitivity {sens_d:.2e})")
+    assert e2e_z <= max(2e-3, 2 * sens_z), "config 3 SiLU end to end"
+    assert e2e <= max(2e-3, 2 * sens_d), "config 3 down end to end"
+    # teacher-forced down projection
+    a_pk = dev.to_dev(frt.frt_operand_pack_host(z["codes"], E, M, Fm))
+    c = _gemm_f32(frt, dev, M, K, Fm, 4, E, frt.W_PLAIN, a_pk, wd, cd, s_z)
+    torch.cuda.synchronize()
+    assert rel_l2(dev.to_np(c), c_down) <= 2e-3
+
+
+# ------------------------------------------------------------------ workload 5
+
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+@pytest.mark.parametrize("M", [1, 10, 16, 32, 50, 64])
+def test_config5_gate_up_sweep(F, M, dtype):
+    frt, dev = F
+    w5 = synth.workload5(M)
+    K, N, eps = w5["K"], w5["N"], w5["eps"]
+    dt = frt.DTYPES[dtype]
+    w_v = codec.bf16_decode(w5["w"])
+    if dtype == "e4m3":
+        cal = synth.workload5(M, seed=synth.CAL_SEED)
+        s_y, s_z = ref.calibrate_block(cal["r"], cal["x"], None, None, None, w_v, eps)
+    else:
+        s_y = s_z = 1.0
+    wp, cs = dev.pack_weight(w5["w"], dt, frt.W_GATE_UP)
+    op = _producer(frt, dev, M, K, w5["r"], w5["x"], None, None, None, eps, dt, s_y)
+    s_tab = frt.frt_splitk_choose(M, N, K, dt)
+    parts = dev.empty_f32(s_tab, M, N)
+    frt.frt_skinny_gemm_splitk(M, N, K, 0, dt, frt.W_GATE_UP, op, wp, cs, s_y, parts, parts.numel() * 4,
+                               frt.EPI_NONE, None, dt, 1.0)
+    zo = _silu(frt, dev, M, N, K, 1, dt, op, wp, cs, s_y, s_z)
+    torch.cuda.synchronize()
+    o = ref.residual_norm_quant(w5["r"], w5["x"][None], None, 1.0, None, None, None, eps, dtype, s_y)
+    wc, ws, _ = ref.pack_weight_values(w_v, None, dtype)
+    c = ref.reduce_partials(ref.gemm_splitk(o["deq"], codec.decode(wc, dtype), 1), s_y, ws)
+    z = ref.silu_gate_quant(c, dtype, s_z)
+    check_codes(dev.operand_codes(op, dt, _mp(M), K)[:M], o["v"], o["mag"], dtype, label=f"config 5 operand M={M}")
+    # the partials of the table's split, reduced on the host in split order, give C
+    p = dev.to_np(parts).astype(np.float64)
+    got = ref.reduce_partials(p, s_y, ws)
+    bar = 5e-3 if dtype == "bf16" else 2e-3
+    assert rel_l2(got, c) <= bar, f"C from s={s_tab} partials"
+    zc = dev.operand_codes(zo, dt, _mp(M), N // 2)
+    assert np.all(zc[M:] == 0)
+    e2e = rel_l2(codec.decode(zc[:M], dtype), z["deq"])
+    assert e2e <= bar, f"config 5 SiLU M={M} end to end"
+    _silu_teacher_forced(frt, dev, M, N, K, 1, dt, dtype, o, wp, cs, codec.decode(wc, dtype), ws, s_y, s_z,
+                         f"config 5 SiLU M={M} {dtype}")
+    print(f"config 5 M={M} {dtype}: split {s_tab}, C rel L2 {rel_l2(got, c):.2e}, SiLU output rel L2 {e2e:.2e}")

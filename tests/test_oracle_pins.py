@@ -404,6 +404,28 @@ def test_calibration_scales_cover_the_calibration_run():
     assert sc[0, 0] >= float(np.float32(np.max(np.abs(y)) / 448.0))
 
 
+def test_block_calibration_is_the_largest_magnitude_over_448():
+    # brute force on a tiny block: walk every element of the un-quantised run by hand
+    rng = np.random.default_rng(5)
+    M, K, F = 3, 8, 4
+    r, x = rng.standard_normal((M, K)), rng.standard_normal((M, K))
+    g, sc, sh = rng.standard_normal(K), 0.3 * rng.standard_normal(K), 0.3 * rng.standard_normal(K)
+    w = rng.standard_normal((K, 2 * F)) / np.sqrt(K)
+    s_y, s_z = ref.calibrate_block(r, x, g, sc, sh, w, 1e-6)
+    big_y = big_z = 0.0
+    for m in range(M):
+        h = [r[m, k] + g[k] * x[m, k] for k in range(K)]
+        rms = np.sqrt(sum(v * v for v in h) / K + 1e-6)
+        y = [h[k] / rms * (1.0 + sc[k]) + sh[k] for k in range(K)]
+        big_y = max(big_y, max(abs(v) for v in y))
+        for n in range(F):
+            gt = sum(y[k] * w[k, n] for k in range(K))
+            up = sum(y[k] * w[k, F + n] for k in range(K))
+            big_z = max(big_z, abs(gt / (1.0 + np.exp(-gt)) * up))
+    assert s_y == float(np.float32(big_y / 448.0))
+    assert abs(s_z - big_z / 448.0) <= 2.0 ** -23 * s_z + 1e-15
+
+
 # ------------------------------------------------------------------ the pins catch planted mistakes
 
 def _planted(monkeypatch, obj, name, fn, pin):
