@@ -125,7 +125,13 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
   }
   return e4m3_code(a) | (e4m3_code(b) << 8) | (e4m3_code(c) << 16) | (e4m3_code(d) << 24);
 }
-__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
+// Two values to bf16 with the gfx950 convert (round to nearest even; matches bf16_bits on
+// every non-NaN input).
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_hw){a, b}, bf16x2_hw));
+}
 
 // Single rounding of a float64 value whose float32 rounding may land exactly on a
 // rounding boundary of the narrow format although the float64 value does not (double
@@ -230,7 +236,8 @@ struct GemmParams {
   int M, N, K, MB, splits;
   int ab_dtype, layout;
   int ksteps_per_split;      // K / kstep / splits
-  int kwaves;                // waves per workgroup splitting the chunk
+  int kwaves;                // waves per workgroup splitting the chunk (set at launch)
+  int row_groups, col_groups;  // workgroup grid per split (set at launch)
   const uint8_t* a;
   const uint8_t* w;
   const float* colscale;
@@ -296,6 +303,5 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 // Library choices of split count and waves per workgroup.
 int choose_splits(int M, int N, int K, int dtype, int epi);
-int choose_kwaves(int ksteps_per_split, int frags);
 
 }  // namespace frt

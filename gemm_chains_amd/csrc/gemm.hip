@@ -15,219 +15,9 @@
 // activations come packed the same way from the producer.  A workgroup owns NT column
 // tiles and one K-chunk; its waves split the chunk's k-steps and are summed through LDS
 // in wave order, so every result is bitwise deterministic.
-#include "frt_internal.hpp"
+#include "gemm_kernel.hpp"
 
 namespace frt {
-
-template <int DT>
-struct Frag;
-template <>
-struct Frag<FRT_BF16> {
-  u32x4 v;
-};
-template <>
-struct Frag<FRT_E4M3> {
-  u32x4 v0, v1;
-};
-
-template <int DT>
-__device__ __forceinline__ void load_frag(Frag<DT>& f, const uint8_t* tile, int lane, bool stream);
-template <>
-__device__ __forceinline__ void load_frag<FRT_BF16>(Frag<FRT_BF16>& f, const uint8_t* tile, int lane,
-                                                    bool stream) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(tile + lane * 16);
-  f.v = stream ? __builtin_nontemporal_load(p) : *p;
-}
-template <>
-__device__ __forceinline__ void load_frag<FRT_E4M3>(Frag<FRT_E4M3>& f, const uint8_t* tile, int lane,
-                                                    bool stream) {
-  const u32x4* p0 = reinterpret_cast<const u32x4*>(tile + lane * 16);
-  const u32x4* p1 = reinterpret_cast<const u32x4*>(tile + 1024 + lane * 16);
-  if (stream) {
-    f.v0 = __builtin_nontemporal_load(p0);
-    f.v1 = __builtin_nontemporal_load(p1);
-  } else {
-    f.v0 = *p0;
-    f.v1 = *p1;
-  }
-}
-
-__device__ __forceinline__ f32x4 mma(const Frag<FRT_BF16>& w, const Frag<FRT_BF16>& a, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w.v),
-                                                 __builtin_bit_cast(bf16x8, a.v), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma(const Frag<FRT_E4M3>& w, const Frag<FRT_E4M3>& a, f32x4 c) {
-  i32x8 wa, aa;
-  wa[0] = (int)w.v0.x; wa[1] = (int)w.v0.y; wa[2] = (int)w.v0.z; wa[3] = (int)w.v0.w;
-  wa[4] = (int)w.v1.x; wa[5] = (int)w.v1.y; wa[6] = (int)w.v1.z; wa[7] = (int)w.v1.w;
-  aa[0] = (int)a.v0.x; aa[1] = (int)a.v0.y; aa[2] = (int)a.v0.z; aa[3] = (int)a.v0.w;
-  aa[4] = (int)a.v1.x; aa[5] = (int)a.v1.y; aa[6] = (int)a.v1.z; aa[7] = (int)a.v1.w;
-  // format 0/0 = OCP e4m3 for both operands; E8M0 block scales 127 = 2^0 (unscaled)
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, aa, c, 0, 0, 0, 127, 0, 127);
-}
-
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
-
-// Epilogue for one 16x16 accumulator fragment when the whole K was summed in this kernel.
-// v[r] = C^T[n0 + r][m] for lane-owned (m, n0..n0+3).
-__device__ __forceinline__ void store_c4(const GemmParams& p, int m, int n0, f32x4 v, float as) {
-  if (m >= p.M) return;
-  f32x4 c = v * as;
-  if (p.colscale) c *= *reinterpret_cast<const f32x4*>(p.colscale + n0);
-  if (p.epi == kEpiQkv) {
-    store_qkv4(p.q_out, p.k_out, p.v_out, p.nq, p.hd, p.v_ld, m, n0, c);
-  } else if (p.epi == FRT_EPI_STORE_F32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (size_t)m * p.N + n0) = c;
-  } else {
-    u32x2 w;
-    w.x = bf16_pack2(c.x, c.y);
-    w.y = bf16_pack2(c.z, c.w);
-    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + (size_t)m * p.N + n0) = w;
-  }
-}
-
-template <int DT, int MB, int NT>
-__global__ void __launch_bounds__(512) skinny_gemm_kernel(const GemmParams p) {
-  constexpr int TB = DT == FRT_BF16 ? 1024 : 2048;
-  // k-steps per pipeline stage: two stages of (NT + MB) fragments plus the accumulators
-  // should stay within ~160 VGPRs so that two waves fit per SIMD without spills
-  constexpr int NV = DT == FRT_BF16 ? 1 : 2;
-  constexpr int U_fit = (160 - 4 * NT * MB) / (2 * (NT + MB) * 4 * NV);
-  constexpr int U = U_fit < 1 ? 1 : (U_fit > 4 ? 4 : U_fit);
-  extern __shared__ f32x4 red[];  // [kwaves][NT*MB][64]
-
-  const int lane = threadIdx.x & 63;
-  // wave index made provably uniform: MFMAs ignore EXEC, so every branch around them must
-  // be a scalar branch, never an EXEC-masked one
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kw = p.kwaves;
-  const int g = blockIdx.x;        // column-tile group: packed tiles [g*NT, g*NT + NT)
-  const int split = blockIdx.y;
-  const int KS = p.K / (DT == FRT_BF16 ? 32 : 128);
-  const int per = p.ksteps_per_split / kw;
-  const int ks_begin = split * p.ksteps_per_split + wave * per;
-  const int ks_end = ks_begin + per;
-
-  const uint8_t* wbase[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) wbase[t] = p.w + (size_t)(g * NT + t) * KS * TB;
-
-  f32x4 acc[NT][MB];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int b = 0; b < MB; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  Frag<DT> wf[2][U][NT];
-  Frag<DT> af[2][U][MB];
-  auto load_stage = [&](int buf, int ks0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ks = ks0 + u;
-      if (ks < ks_end) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) load_frag<DT>(wf[buf][u][t], wbase[t] + (size_t)ks * TB, lane, true);
-#pragma unroll
-        for (int b = 0; b < MB; ++b)
-          load_frag<DT>(af[buf][u][b], p.a + ((size_t)ks * MB + b) * TB, lane, false);
-      }
-    }
-  };
-  auto compute_stage = [&](int buf, int ks0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ks0 + u < ks_end) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int b = 0; b < MB; ++b) acc[t][b] = mma(wf[buf][u][t], af[buf][u][b], acc[t][b]);
-      }
-    }
-  };
-
-  // two-stage register pipeline: stage i+1's loads are in flight while stage i computes
-  if (ks_begin < ks_end) load_stage(0, ks_begin);
-  for (int ks0 = ks_begin; ks0 < ks_end; ks0 += 2 * U) {
-    if (ks0 + U < ks_end) load_stage(1, ks0 + U);
-    compute_stage(0, ks0);
-    if (ks0 + U < ks_end) {
-      if (ks0 + 2 * U < ks_end) load_stage(0, ks0 + 2 * U);
-      compute_stage(1, ks0 + U);
-    }
-  }
-
-  const float as = load_scale(p.act_scale_ptr, p.act_scale);
-  const bool partial_out = (p.epi == FRT_EPI_NONE) || p.splits > 1;
-  constexpr int NF = NT * MB;
-
-  // combine the kw waves' sums in wave order (LDS), then each wave finishes some fragments
-  if (kw > 1) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int b = 0; b < MB; ++b) red[((size_t)wave * NF + t * MB + b) * 64 + lane] = acc[t][b];
-    __syncthreads();
-  }
-
-  auto finish = [&](int t, int b, f32x4 v) {
-    const int lt = logical_tile_of(p.layout, p.N, g * NT + t);
-    const int n0 = lt * 16 + 4 * (lane >> 4);
-    const int m = b * 16 + (lane & 15);
-    if (partial_out) {
-      if (m < p.M) *reinterpret_cast<f32x4*>(p.partials + ((size_t)split * p.M + m) * p.N + n0) = v;
-    } else {
-      store_c4(p, m, n0, v, as);
-    }
-  };
-  const float os = load_scale(p.out_scale_ptr, p.out_scale);
-  // SiLU-gate epilogue: packed tiles 2i (gate) and 2i+1 (up) of this workgroup pair up
-  auto finish_pair = [&](int tp, int b, f32x4 vg, f32x4 vu) {
-    const int ng = logical_tile_of(p.layout, p.N, g * NT + 2 * tp) * 16 + 4 * (lane >> 4);
-    const int nu = logical_tile_of(p.layout, p.N, g * NT + 2 * tp + 1) * 16 + 4 * (lane >> 4);
-    const int m = b * 16 + (lane & 15);
-    f32x4 cg = vg * as, cu = vu * as;
-    if (p.colscale) {
-      cg *= *reinterpret_cast<const f32x4*>(p.colscale + ng);
-      cu *= *reinterpret_cast<const f32x4*>(p.colscale + nu);
-    }
-    float z[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = silu_f(cg[r]) * cu[r];
-    store_operand4(reinterpret_cast<uint8_t*>(p.out), p.out_dtype, MB, m, ng, z[0], z[1], z[2], z[3], os,
-                   m >= p.M);
-    if (m < p.M) record_amax(p.amax, z[0], z[1], z[2], z[3]);
-  };
-  const bool silu = !partial_out && p.epi == FRT_EPI_SILU_GATE_QUANT;
-
-  if (kw == 1) {
-    if (silu) {
-#pragma unroll
-      for (int tp = 0; tp < NT / 2; ++tp)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) finish_pair(tp, b, acc[2 * tp][b], acc[2 * tp + 1][b]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) finish(t, b, acc[t][b]);
-    }
-    return;
-  }
-  auto sum_waves = [&](int f) {
-    f32x4 v = red[(size_t)f * 64 + lane];
-    for (int w2 = 1; w2 < kw; ++w2) v += red[((size_t)w2 * NF + f) * 64 + lane];
-    return v;
-  };
-  if (silu) {
-    constexpr int NPAIR = (NT / 2) * MB;
-    for (int f = wave; f < NPAIR; f += kw) {
-      const int tp = f / MB, b = f % MB;
-      finish_pair(tp, b, sum_waves((2 * tp) * MB + b), sum_waves((2 * tp + 1) * MB + b));
-    }
-  } else {
-    for (int f = wave; f < NF; f += kw) finish(f / MB, f % MB, sum_waves(f));
-  }
-}
 
 // Consumer: fixed-order split-K reduction + scale recovery + epilogue.  One thread per
 // 4 consecutive columns of one row (rows up to Mp for the SiLU epilogue, whose padding
@@ -286,61 +76,58 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceParams p
 }
 
 // ------------------------------------------------------------------ launch plumbing
-template <int DT, int MB, int NT>
-static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
-  const int groups = p.N / 16 / NT;
-  const size_t lds = p.kwaves > 1 ? (size_t)p.kwaves * NT * MB * 64 * sizeof(f32x4) : 0;
-  hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT>), dim3(groups, p.splits), dim3(64 * p.kwaves), lds, s, p);
-  return hipGetLastError();
+// Frag registers per lane: 4 (bf16) or 8 (e4m3) per tile per k-step.  A round's loads
+// stay within ~192 VGPRs so that every one of them can be in flight at once.
+static int per_max(int dtype, int nt, int mbw) {
+  const int v = dtype == FRT_BF16 ? 4 : 8;
+  int per = 8;
+  while (per > 1 && per * (nt + mbw) * v > 192) per /= 2;
+  return per;
 }
 
-template <int DT, int MB>
-static hipError_t launch_nt(const GemmParams& p, int nt, hipStream_t s) {
-  switch (nt) {
-    case 1: return launch_t<DT, MB, 1>(p, s);
-    case 2: return launch_t<DT, MB, 2>(p, s);
-    default: return launch_t<DT, MB, 4>(p, s);
-  }
-}
-
-template <int DT>
-static hipError_t launch_mb(const GemmParams& p, int nt, hipStream_t s) {
-  switch (p.MB) {
-    case 1: return launch_nt<DT, 1>(p, nt, s);
-    case 2: return launch_nt<DT, 2>(p, nt, s);
-    case 3: return launch_nt<DT, 3>(p, nt, s);
-    default: return launch_nt<DT, 4>(p, nt, s);
-  }
-}
-
-// Column tiles per workgroup: the SiLU epilogue needs gate/up pairs (even NT); otherwise
-// pick the widest tile group that still leaves >= 256 workgroups (one per CU).
-static int choose_nt(const GemmParams& p) {
+// Measured on MI355X at the action-decoder shapes (M = 10/50, K = 1024..4096):
+//  - widest column group (NT = 4, 2, 1) that still leaves >= 256 workgroups; the SiLU
+//    epilogue needs gate/up pairs (even NT);
+//  - when even the narrowest group leaves fewer than 256 workgroups, the row blocks are
+//    spread over row groups (one block each) on the column group's XCD;
+//  - four waves per workgroup, each with as many k-steps per round as its registers
+//    allow (eight waves with shorter runs lose to the longer LDS merge).
+static GemmShape choose_shape(const GemmParams& p) {
+  GemmShape sh{};
   const int tiles = p.N / 16;
-  const bool pairs = p.splits == 1 && p.epi == FRT_EPI_SILU_GATE_QUANT;
-  int nt = pairs ? 2 : 1;
+  const bool partial = p.epi == FRT_EPI_NONE || p.splits > 1;
+  if (partial) sh.epi = kGemmPartial;
+  else if (p.epi == FRT_EPI_SILU_GATE_QUANT) sh.epi = p.out_dtype == FRT_BF16 ? kGemmSiluBf16 : kGemmSiluE4m3;
+  else sh.epi = p.epi == kEpiQkv ? kGemmQkv : kGemmStore;
+  const int nt_min = sh.epi == kGemmSiluBf16 || sh.epi == kGemmSiluE4m3 ? 2 : 1;
+  sh.nt = nt_min;
   for (int cand : {4, 2}) {
-    if (tiles % cand) continue;
-    if (pairs && cand % 2) continue;
-    if ((tiles / cand) * p.splits >= 256) { nt = cand > nt ? cand : nt; break; }
+    if (tiles % cand || cand < nt_min) continue;
+    if ((tiles / cand) * p.splits >= 256) { sh.nt = cand; break; }
   }
-  if (tiles % nt) nt = 1;
-  return nt;
-}
-
-// Waves per workgroup splitting a K-chunk: up to 8, dividing the chunk's k-steps, and
-// keeping the cross-wave LDS buffer (kw * frags * 1 KB) within 64 KB.
-int choose_kwaves(int ksteps_per_split, int frags) {
-  int kw = 1;
-  while (kw < 8 && ksteps_per_split % (kw * 2) == 0 && (kw * 2) * frags <= 64) kw *= 2;
-  return kw;
+  if (tiles % sh.nt) sh.nt = 1;
+  sh.col_groups = tiles / sh.nt;
+  sh.mbw = p.MB;
+  sh.row_groups = 1;
+  if (sh.col_groups * p.splits < 256 && p.MB > 1) {
+    sh.mbw = 1;
+    sh.row_groups = p.MB;
+  }
+  const int kps = p.ksteps_per_split;
+  sh.kw = kps % 4 == 0 ? 4 : (kps % 2 == 0 ? 2 : 1);
+  const int run = kps / sh.kw;
+  sh.per = per_max(p.ab_dtype, sh.nt, sh.mbw);
+  while (sh.per > 1 && run % sh.per) sh.per /= 2;
+  return sh;
 }
 
 hipError_t launch_gemm(const GemmParams& p_in, hipStream_t s) {
   GemmParams p = p_in;
-  const int nt = choose_nt(p);
-  p.kwaves = choose_kwaves(p.ksteps_per_split, nt * p.MB);
-  return p.ab_dtype == FRT_BF16 ? launch_mb<FRT_BF16>(p, nt, s) : launch_mb<FRT_E4M3>(p, nt, s);
+  const GemmShape sh = choose_shape(p);
+  p.kwaves = sh.kw;
+  p.row_groups = sh.row_groups;
+  p.col_groups = sh.col_groups;
+  return p.ab_dtype == FRT_BF16 ? launch_gemm_typed<FRT_BF16>(p, sh, s) : launch_gemm_typed<FRT_E4M3>(p, sh, s);
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {

@@ -1,0 +1,276 @@
+// Skinny split-K GEMM kernel template (instantiated per operand type in gemm_bf16.hip
+// and gemm_e4m3.hip; host side in gemm.hip).
+//
+// Pages: observation-age notes ("思考探索：具身推理加速，先看动作执行时观测有多旧"),
+// section "小 M GEMM 要看并行度，也要看归约代价" (C = A W with few rows, cut along K into
+// FP32 partial products that a consumer reduces), section "静态量化改变了两次矩阵乘之间的工作"
+// (the GEMM's scale recovery remains after static quantisation).
+//
+// Mapping (gfx950): the weight tile is the MFMA's A operand (16 output columns x one
+// k-step) and the activation tile its B operand (one k-step x 16 action rows), so the
+// 16x16 accumulator holds C^T for 16 columns x 16 rows and M (<= 64) occupies 1..4
+// column blocks.  Weights are pre-packed so that one 16-byte load per lane is one tile
+// (1 KB per wave load, fully coalesced, straight into VGPRs with no LDS round trip);
+// activations come packed the same way from the producer.
+//
+// Every launch starts with a cold instruction cache, so each kernel carries only the
+// code of its own epilogue (a template parameter): a long branchy tail costs fetch
+// latency on every launch.
+#pragma once
+#include "frt_internal.hpp"
+
+namespace frt {
+
+enum GemmEpi { kGemmPartial = 0, kGemmStore = 1, kGemmSiluBf16 = 2, kGemmSiluE4m3 = 3, kGemmQkv = 4 };
+
+// Tile shape of a launch: NT column tiles and MB row blocks per workgroup, kw waves with
+// PER k-steps per round; (col_groups x row_groups) workgroups per split.
+struct GemmShape {
+  int nt, mbw, per, kw, col_groups, row_groups, epi;
+};
+
+template <int DT>
+struct Frag;
+template <>
+struct Frag<FRT_BF16> {
+  u32x4 v;
+};
+template <>
+struct Frag<FRT_E4M3> {
+  u32x4 v0, v1;
+};
+
+// One MFMA operand tile per wave: 16 bytes per lane (bf16) or two 16-byte halves (e4m3).
+// STREAM marks weight loads non-temporal so the single-use weight stream does not evict
+// the activation tiles every workgroup re-reads from L2.  (A compile-time choice: two
+// loads of one address behind a run-time select get merged and lose the hint.)
+template <int DT, bool STREAM>
+__device__ __forceinline__ void load_frag(Frag<DT>& f, const uint8_t* tile, int lane) {
+  const u32x4* p0 = reinterpret_cast<const u32x4*>(tile + lane * 16);
+  if constexpr (DT == FRT_BF16) {
+    if constexpr (STREAM) f.v = __builtin_nontemporal_load(p0);
+    else f.v = *p0;
+  } else {
+    const u32x4* p1 = reinterpret_cast<const u32x4*>(tile + 1024 + lane * 16);
+    if constexpr (STREAM) {
+      f.v0 = __builtin_nontemporal_load(p0);
+      f.v1 = __builtin_nontemporal_load(p1);
+    } else {
+      f.v0 = *p0;
+      f.v1 = *p1;
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4 mma(const Frag<FRT_BF16>& w, const Frag<FRT_BF16>& a, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w.v),
+                                                 __builtin_bit_cast(bf16x8, a.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<FRT_E4M3>& w, const Frag<FRT_E4M3>& a, f32x4 c) {
+  i32x8 wa, aa;
+  wa[0] = (int)w.v0.x; wa[1] = (int)w.v0.y; wa[2] = (int)w.v0.z; wa[3] = (int)w.v0.w;
+  wa[4] = (int)w.v1.x; wa[5] = (int)w.v1.y; wa[6] = (int)w.v1.z; wa[7] = (int)w.v1.w;
+  aa[0] = (int)a.v0.x; aa[1] = (int)a.v0.y; aa[2] = (int)a.v0.z; aa[3] = (int)a.v0.w;
+  aa[4] = (int)a.v1.x; aa[5] = (int)a.v1.y; aa[6] = (int)a.v1.z; aa[7] = (int)a.v1.w;
+  // format 0/0 = OCP e4m3 for both operands; E8M0 block scales 127 = 2^0 (unscaled)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, aa, c, 0, 0, 0, 127, 0, 127);
+}
+
+// SiLU(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (a few ulp; the parity
+// tie band is 2^-17 of the summands).
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
+// Workgroup = (column-tile group g, row group r, K-chunk `split`).  Its kw waves split the
+// chunk's k-steps into contiguous runs of PER * rounds; in each round a wave issues all
+// of its PER k-steps' weight and activation loads before its first wait (a scheduling
+// barrier keeps the compiler from interleaving them with the MFMAs, which would put a
+// memory round trip between every few MFMAs), then runs the MFMAs.  The waves' sums are
+// added in LDS in wave order, so results are bitwise deterministic and independent of
+// the row grouping.  Row groups (XCD-aware: the groups that share a column group are
+// eight workgroup ids apart, so they run on one XCD and its L2 serves the weight tile
+// to all of them after one HBM read) spread GEMMs with few column tiles over more CUs.
+template <int DT, int MB, int NT, int PER, int EPI>
+__global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
+  constexpr int TB = DT == FRT_BF16 ? 1024 : 2048;
+  constexpr int NF = NT * MB;
+  extern __shared__ f32x4 red[];  // [kwaves][NF][64]
+
+  const int lane = threadIdx.x & 63;
+  // wave index made provably uniform: MFMAs ignore EXEC, so every branch around them must
+  // be a scalar branch, never an EXEC-masked one
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kw = p.kwaves;
+  int g, r;
+  if (p.row_groups == 1) {
+    g = blockIdx.x;
+    r = 0;
+  } else {
+    const int L = blockIdx.x, R = p.row_groups;
+    g = (L / (8 * R)) * 8 + (L & 7);
+    r = (L >> 3) % R;
+    if (g >= p.col_groups) return;  // padding of the XCD-aware grid (whole workgroup)
+  }
+  const int mb0 = r * MB;  // first 16-row block of this workgroup
+  const int split = blockIdx.y;
+  const int KS = p.K / (DT == FRT_BF16 ? 32 : 128);
+  const int run = p.ksteps_per_split / kw;  // = PER * rounds
+  const int ks_begin = split * p.ksteps_per_split + wave * run;
+
+  const uint8_t* wbase[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) wbase[t] = p.w + (size_t)(g * NT + t) * KS * TB;
+  const uint8_t* abase = p.a + (size_t)mb0 * TB;
+  const size_t astep = (size_t)p.MB * TB;
+
+  f32x4 acc[NT][MB];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ks0 = ks_begin; ks0 < ks_begin + run; ks0 += PER) {
+    Frag<DT> wf[PER][NT];
+    Frag<DT> af[PER][MB];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) load_frag<DT, true>(wf[u][t], wbase[t] + (size_t)(ks0 + u) * TB, lane);
+#pragma unroll
+      for (int b = 0; b < MB; ++b) load_frag<DT, false>(af[u][b], abase + (size_t)(ks0 + u) * astep + (size_t)b * TB, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[t][b] = mma(wf[u][t], af[u][b], acc[t][b]);
+  }
+
+  // ---- epilogue (one per kernel)
+  const float as = load_scale(p.act_scale_ptr, p.act_scale);
+  // fragment (t, b) finished: partial store, or scale recovery + store / Q-K-V scatter
+  auto finish = [&](int t, int b, f32x4 v) {
+    const int n0 = logical_tile_of(p.layout, p.N, g * NT + t) * 16 + 4 * (lane >> 4);
+    const int m = (mb0 + b) * 16 + (lane & 15);
+    if (m >= p.M) return;
+    if constexpr (EPI == kGemmPartial) {
+      *reinterpret_cast<f32x4*>(p.partials + ((size_t)split * p.M + m) * p.N + n0) = v;
+    } else {
+      f32x4 c = v * as;
+      if (p.colscale) c *= *reinterpret_cast<const f32x4*>(p.colscale + n0);
+      if constexpr (EPI == kGemmQkv) {
+        store_qkv4(p.q_out, p.k_out, p.v_out, p.nq, p.hd, p.v_ld, m, n0, c);
+      } else if (p.epi == FRT_EPI_STORE_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + (size_t)m * p.N + n0) = c;
+      } else {
+        u32x2 w;
+        w.x = bf16_pack2(c.x, c.y);
+        w.y = bf16_pack2(c.z, c.w);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + (size_t)m * p.N + n0) = w;
+      }
+    }
+  };
+  // SiLU-gate epilogue: packed tiles 2i (gate) and 2i+1 (up) of this workgroup pair up;
+  // padding rows of the output operand get zero codes
+  auto finish_pair = [&](int tp, int b, f32x4 vg, f32x4 vu) {
+    const int ng = logical_tile_of(p.layout, p.N, g * NT + 2 * tp) * 16 + 4 * (lane >> 4);
+    const int nu = logical_tile_of(p.layout, p.N, g * NT + 2 * tp + 1) * 16 + 4 * (lane >> 4);
+    const int m = (mb0 + b) * 16 + (lane & 15);
+    f32x4 cg = vg * as, cu = vu * as;
+    if (p.colscale) {
+      cg *= *reinterpret_cast<const f32x4*>(p.colscale + ng);
+      cu *= *reinterpret_cast<const f32x4*>(p.colscale + nu);
+    }
+    float z[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = silu_f(cg[e]) * cu[e];
+    const float os = load_scale(p.out_scale_ptr, p.out_scale);
+    store_operand4(reinterpret_cast<uint8_t*>(p.out), EPI == kGemmSiluBf16 ? FRT_BF16 : FRT_E4M3, p.MB, m, ng,
+                   z[0], z[1], z[2], z[3], os, m >= p.M);
+    if (m < p.M) record_amax(p.amax, z[0], z[1], z[2], z[3]);
+  };
+
+  // combine the kw (<= 4) waves' sums in wave order through LDS (with one wave too: a
+  // loop over LDS is far shorter code than unrolling every fragment's epilogue)
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) red[((size_t)wave * NF + t * MB + b) * 64 + lane] = acc[t][b];
+  __syncthreads();
+  auto sum_waves = [&](int f) {
+    f32x4 v = red[(size_t)f * 64 + lane];
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2)
+      if (w2 < kw) v += red[((size_t)w2 * NF + f) * 64 + lane];
+    return v;
+  };
+  if constexpr (EPI == kGemmSiluBf16 || EPI == kGemmSiluE4m3) {
+    constexpr int NPAIR = (NT / 2) * MB;
+    for (int f = wave; f < NPAIR; f += kw) {
+      const int tp = f / MB, b = f % MB;
+      finish_pair(tp, b, sum_waves((2 * tp) * MB + b), sum_waves((2 * tp + 1) * MB + b));
+    }
+  } else {
+    for (int f = wave; f < NF; f += kw) finish(f / MB, f % MB, sum_waves(f));
+  }
+}
+
+// ------------------------------------------------------------------ typed dispatch
+template <int DT, int MB, int NT, int PER, int EPI>
+static hipError_t launch_t(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
+  constexpr bool silu = EPI == kGemmSiluBf16 || EPI == kGemmSiluE4m3;
+  if constexpr (PER * (NT + MB) * (DT == FRT_BF16 ? 4 : 8) > 192 || (silu && NT % 2)) {
+    return hipErrorInvalidValue;  // never chosen (register budget / SiLU pairs): not instantiated
+  } else {
+    const int grid_x = sh.row_groups == 1 ? sh.col_groups : (sh.col_groups + 7) / 8 * 8 * sh.row_groups;
+    const size_t lds = (size_t)p.kwaves * NT * MB * 64 * sizeof(f32x4);
+    hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI>), dim3(grid_x, p.splits), dim3(64 * p.kwaves),
+                       lds, s, p);
+    return hipGetLastError();
+  }
+}
+
+template <int DT, int MB, int NT, int PER>
+static hipError_t launch_epi(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
+  switch (sh.epi) {
+    case kGemmPartial: return launch_t<DT, MB, NT, PER, kGemmPartial>(p, sh, s);
+    case kGemmStore: return launch_t<DT, MB, NT, PER, kGemmStore>(p, sh, s);
+    case kGemmSiluBf16: return launch_t<DT, MB, NT, PER, kGemmSiluBf16>(p, sh, s);
+    case kGemmSiluE4m3: return launch_t<DT, MB, NT, PER, kGemmSiluE4m3>(p, sh, s);
+    default: return launch_t<DT, MB, NT, PER, kGemmQkv>(p, sh, s);
+  }
+}
+
+template <int DT, int MB, int NT>
+static hipError_t launch_per(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
+  switch (sh.per) {
+    case 1: return launch_epi<DT, MB, NT, 1>(p, sh, s);
+    case 2: return launch_epi<DT, MB, NT, 2>(p, sh, s);
+    case 4: return launch_epi<DT, MB, NT, 4>(p, sh, s);
+    default: return launch_epi<DT, MB, NT, 8>(p, sh, s);
+  }
+}
+
+template <int DT, int MB>
+static hipError_t launch_nt(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
+  switch (sh.nt) {
+    case 1: return launch_per<DT, MB, 1>(p, sh, s);
+    case 2: return launch_per<DT, MB, 2>(p, sh, s);
+    default: return launch_per<DT, MB, 4>(p, sh, s);
+  }
+}
+
+template <int DT>
+hipError_t launch_gemm_typed(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
+  switch (sh.mbw) {
+    case 1: return launch_nt<DT, 1>(p, sh, s);
+    case 2: return launch_nt<DT, 2>(p, sh, s);
+    case 3: return launch_nt<DT, 3>(p, sh, s);
+    default: return launch_nt<DT, 4>(p, sh, s);
+  }
+}
+
+}  // namespace frt
