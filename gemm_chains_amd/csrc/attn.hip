@@ -125,15 +125,13 @@ __device__ __forceinline__ void attend_block(const KVBlock& b, const bf16x8 (&qf
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float a0 = pr[2 * j], a1 = pr[2 * j + 1];
-    const uint32_t h0 = bf16_bits(a0), h1 = bf16_bits(a1);
-    a0 -= bf16_to_f32(h0);
-    a1 -= bf16_to_f32(h1);
-    const uint32_t m0 = bf16_bits(a0), m1 = bf16_bits(a1);
-    a0 -= bf16_to_f32(m0);
-    a1 -= bf16_to_f32(m1);
-    hi[j] = h0 | (h1 << 16);
-    mid[j] = m0 | (m1 << 16);
-    lo[j] = bf16_bits(a0) | (bf16_bits(a1) << 16);
+    hi[j] = bf16_pack2(a0, a1);
+    a0 -= bf16_to_f32(hi[j]);
+    a1 -= bf16_to_f32(hi[j] >> 16);
+    mid[j] = bf16_pack2(a0, a1);
+    a0 -= bf16_to_f32(mid[j]);
+    a1 -= bf16_to_f32(mid[j] >> 16);
+    lo[j] = bf16_pack2(a0, a1);
   }
   const bf16x8 phi = bf16x8_from(hi), pmid = bf16x8_from(mid), plo = bf16x8_from(lo);
   // keys past the sequence: zero their V entries (the clamped or padded loads are finite
@@ -161,7 +159,7 @@ __device__ __forceinline__ void attend_block(const KVBlock& b, const bf16x8 (&qf
 // 32-key blocks of the chunk, each keeping an online softmax with the next block's loads
 // in flight while the current one is computed; the waves merge in wave order.  With one
 // chunk the workgroup writes the quantised output, otherwise an fp32 partial record.
-template <int NW, bool MULTI>
+template <int NW, bool MULTI, bool REC, int ODT>
 __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p) {
   const int h = blockIdx.x, mb = blockIdx.y, ch = blockIdx.z, nch = gridDim.z;
   // wave index made provably uniform: MFMAs ignore EXEC, so branches around them must be
@@ -238,15 +236,15 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
     const int d = d0 + e4, dt = d >> 4, lg = (d & 15) >> 2;   // 4 d sit in one accumulator of one lane
     f32x4 acc = comb[0][dt][lg * 16 + tq] * wgt[0];
     for (int w = 1; w < NW; ++w) acc += comb[w][dt][lg * 16 + tq] * wgt[w];
-    if (nch == 1) {
+    if constexpr (!REC) {
       const f32x4 ov = acc / den;
-      store_operand4(p.operand, p.out_dtype, MB, m, h * HD + d, ov.x, ov.y, ov.z, ov.w, os, m >= M);
+      store_operand4(p.operand, ODT, MB, m, h * HD + d, ov.x, ov.y, ov.z, ov.w, os, m >= M);
       if (m < M) record_amax(p.amax, ov.x, ov.y, ov.z, ov.w);
     } else {
       *reinterpret_cast<f32x4*>(rec + 32 + tq * HD + d) = acc;
     }
   }
-  if (nch > 1 && (threadIdx.x % (128 / DPT)) == 0) {
+  if (REC && (threadIdx.x % (128 / DPT)) == 0) {
     rec[tq] = mx;
     rec[16 + tq] = den;
   }
@@ -256,7 +254,7 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
 // 8 d); chunks in order (deterministic).  With CH > 0 (nch <= CH) every record of the
 // thread is loaded before the first is used, so the records, written by the previous
 // kernel on other XCDs, cost one memory latency instead of one per chunk.
-template <int CH>
+template <int CH, int ODT>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, int nch) {
   const int h = blockIdx.x, mb = blockIdx.y, MB = gridDim.y;
   const int tq = threadIdx.x >> 4;
@@ -304,9 +302,8 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
   const float os = load_scale(p.out_scale_ptr, p.out_scale);
   const int m = mb * 16 + tq;
   const int k = h * HD + d0;
-  store_operand4(p.operand, p.out_dtype, MB, m, k, num[0] / den, num[1] / den, num[2] / den, num[3] / den, os,
-                 m >= p.M);
-  store_operand4(p.operand, p.out_dtype, MB, m, k + 4, num[4] / den, num[5] / den, num[6] / den, num[7] / den, os,
+  store_operand4(p.operand, ODT, MB, m, k, num[0] / den, num[1] / den, num[2] / den, num[3] / den, os, m >= p.M);
+  store_operand4(p.operand, ODT, MB, m, k + 4, num[4] / den, num[5] / den, num[6] / den, num[7] / den, os,
                  m >= p.M);
   if (m < p.M) {
     record_amax(p.amax, num[0] / den, num[1] / den, num[2] / den, num[3] / den);
@@ -314,22 +311,34 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
   }
 }
 
+template <int NW, bool MULTI, bool REC>
+static void launch_chunk(const AttnParams& p, dim3 g, hipStream_t s) {
+  if (REC) hipLaunchKernelGGL((attn_chunk_kernel<NW, MULTI, true, FRT_BF16>), g, dim3(64 * NW), 0, s, p);
+  else if (p.out_dtype == FRT_BF16) hipLaunchKernelGGL((attn_chunk_kernel<NW, MULTI, false, FRT_BF16>), g, dim3(64 * NW), 0, s, p);
+  else hipLaunchKernelGGL((attn_chunk_kernel<NW, MULTI, false, FRT_E4M3>), g, dim3(64 * NW), 0, s, p);
+}
+
+template <int CH>
+static void launch_combine(const AttnParams& p, int nch, hipStream_t s) {
+  const dim3 g(p.n_heads, p.MB), b(256);
+  if (p.out_dtype == FRT_BF16) hipLaunchKernelGGL((attn_combine_kernel<CH, FRT_BF16>), g, b, 0, s, p, nch);
+  else hipLaunchKernelGGL((attn_combine_kernel<CH, FRT_E4M3>), g, b, 0, s, p, nch);
+}
+
 hipError_t launch_attention(const AttnParams& p_in, hipStream_t s) {
   AttnParams p = p_in;
   p.chunk_keys = attention_chunk_keys(p.kv_len);
   const int nch = (p.kv_len + p.chunk_keys - 1) / p.chunk_keys;
-  if (p.chunk_keys <= 128)
-    hipLaunchKernelGGL((attn_chunk_kernel<4, false>), dim3(p.n_heads, p.MB, nch), dim3(256), 0, s, p);
-  else if (p.chunk_keys <= 256)
-    hipLaunchKernelGGL((attn_chunk_kernel<8, false>), dim3(p.n_heads, p.MB, nch), dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_chunk_kernel<8, true>), dim3(p.n_heads, p.MB, nch), dim3(512), 0, s, p);
+  const dim3 g(p.n_heads, p.MB, nch);
+  const bool rec = nch > 1;
+  if (p.chunk_keys <= 128) rec ? launch_chunk<4, false, true>(p, g, s) : launch_chunk<4, false, false>(p, g, s);
+  else if (p.chunk_keys <= 256) rec ? launch_chunk<8, false, true>(p, g, s) : launch_chunk<8, false, false>(p, g, s);
+  else rec ? launch_chunk<8, true, true>(p, g, s) : launch_chunk<8, true, false>(p, g, s);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nch == 1) return e;
-  const dim3 g(p.n_heads, p.MB), b(256);
-  if (nch <= 8) hipLaunchKernelGGL(attn_combine_kernel<8>, g, b, 0, s, p, nch);
-  else if (nch <= 16) hipLaunchKernelGGL(attn_combine_kernel<16>, g, b, 0, s, p, nch);
-  else hipLaunchKernelGGL(attn_combine_kernel<0>, g, b, 0, s, p, nch);
+  if (e != hipSuccess || !rec) return e;
+  if (nch <= 8) launch_combine<8>(p, nch, s);
+  else if (nch <= 16) launch_combine<16>(p, nch, s);
+  else launch_combine<0>(p, nch, s);
   return hipGetLastError();
 }
 

@@ -20,53 +20,59 @@
 
 namespace frt {
 
-constexpr int kRnqGroups = kMaxProducerK / 1024;  // 4-element groups per thread, max
-
-// SPL = number of fp32 partial slices read (0: no x; otherwise a power of two >= x_splits,
-// slices past x_splits are skipped by a uniform predicate).  Every load of a group is
-// issued before the first one is used: the partials come from the previous kernel and
-// sit beyond this XCD's L2, so a serial chain of loads would pay that latency per slice.
-template <int SPL>
+// Kernel variants are compile-time in everything that shapes the code: SPL = number of
+// fp32 partial slices read (0: no x; -1: any count, run-time loop), G = groups of 4
+// elements per thread (K <= 1024 G), ODT = output operand format (0: none).  Every
+// launch fetches its code cold, so each variant carries only its own path.  All of a
+// group's loads are issued before the first is used: the partials come from the previous
+// kernel and sit beyond this XCD's L2.
+template <int SPL, int G, int ODT>
 __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int K = p.K;
   __shared__ float wsum[4];
-  if (m >= p.M) {
+  if (m >= p.M) {  // padding rows of the operand: zero codes (only launched with an operand)
+    if constexpr (ODT != 0) {
 #pragma unroll
-    for (int i = 0; i < kRnqGroups; ++i) {
-      const int k0 = 4 * (tid + 256 * i);
-      if (k0 < K) store_operand4(p.operand, p.out_dtype, p.MB, m, k0, 0.f, 0.f, 0.f, 0.f, 1.f, true);
+      for (int i = 0; i < G; ++i) {
+        const int k0 = 4 * (tid + 256 * i);
+        if (k0 < K) store_operand4(p.operand, ODT, p.MB, m, k0, 0.f, 0.f, 0.f, 0.f, 1.f, true);
+      }
     }
     return;
   }
-  const float xs = load_scale(p.x_scale_ptr, p.x_scale);
   const size_t row = (size_t)m * K;
   const size_t split_stride = (size_t)p.M * K;
 
-  f32x4 h[kRnqGroups];
+  f32x4 h[G];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kRnqGroups; ++i) {
+  for (int i = 0; i < G; ++i) {
     const int k0 = 4 * (tid + 256 * i);
-    if (k0 >= K) break;
+    if (k0 >= K) {
+      h[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      continue;
+    }
     const f32x4 r = *reinterpret_cast<const f32x4*>(p.residual + row + k0);
     f32x4 hv = r;
-    if constexpr (SPL > 0) {
-      f32x4 xp[SPL];
+    if constexpr (SPL != 0) {
+      f32x4 x;
+      if constexpr (SPL > 0) {
+        f32x4 xp[SPL];
 #pragma unroll
-      for (int j = 0; j < SPL; ++j)
-        if (j < p.x_splits) xp[j] = *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
-      const f32x4 cs = p.x_colscale ? *reinterpret_cast<const f32x4*>(p.x_colscale + k0) : f32x4{1.f, 1.f, 1.f, 1.f};
-      const f32x4 gt = p.gate ? *reinterpret_cast<const f32x4*>(p.gate + k0) : f32x4{1.f, 1.f, 1.f, 1.f};
-      f32x4 x = xp[0];
+        for (int j = 0; j < SPL; ++j) xp[j] = *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
+        x = xp[0];
 #pragma unroll
-      for (int j = 1; j < SPL; ++j)
-        if (j < p.x_splits) x += xp[j];  // partials summed in ascending split order
-      x *= xs;                           // then scale recovery
-      if (p.x_colscale) x *= cs;
-      if (p.gate) x *= gt;
+        for (int j = 1; j < SPL; ++j) x += xp[j];  // partials summed in ascending split order
+      } else {
+        x = *reinterpret_cast<const f32x4*>(p.x + row + k0);
+        for (int j = 1; j < p.x_splits; ++j) x += *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
+      }
+      x *= load_scale(p.x_scale_ptr, p.x_scale);  // then scale recovery
+      if (p.x_colscale) x *= *reinterpret_cast<const f32x4*>(p.x_colscale + k0);
+      if (p.gate) x *= *reinterpret_cast<const f32x4*>(p.gate + k0);
       hv = r + x;
     }
     h[i] = hv;
@@ -75,42 +81,60 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
   }
   if (p.residual_out) {
 #pragma unroll
-    for (int i = 0; i < kRnqGroups; ++i) {
+    for (int i = 0; i < G; ++i) {
       const int k0 = 4 * (tid + 256 * i);
-      if (k0 >= K) break;
-      *reinterpret_cast<f32x4*>(p.residual_out + row + k0) = h[i];
+      if (k0 < K) *reinterpret_cast<f32x4*>(p.residual_out + row + k0) = h[i];
     }
   }
-  if (!p.operand) return;
+  if constexpr (ODT != 0) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if (lane == 0) wsum[wave] = ss;
-  __syncthreads();
-  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-  const float inv = 1.0f / sqrtf(tot / (float)K + p.eps);
-  const float as = load_scale(p.act_scale_ptr, p.act_scale);
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if (lane == 0) wsum[wave] = ss;
+    __syncthreads();
+    const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    const float inv = 1.0f / sqrtf(tot / (float)K + p.eps);
+    const float as = load_scale(p.act_scale_ptr, p.act_scale);
 #pragma unroll
-  for (int i = 0; i < kRnqGroups; ++i) {
-    const int k0 = 4 * (tid + 256 * i);
-    if (k0 >= K) break;
-    f32x4 y = h[i] * inv;
-    if (p.ada_scale) y = y * (1.0f + *reinterpret_cast<const f32x4*>(p.ada_scale + k0));
-    if (p.ada_shift) y = y + *reinterpret_cast<const f32x4*>(p.ada_shift + k0);
-    store_operand4(p.operand, p.out_dtype, p.MB, m, k0, y.x, y.y, y.z, y.w, as, false);
-    record_amax(p.amax, y.x, y.y, y.z, y.w);
+    for (int i = 0; i < G; ++i) {
+      const int k0 = 4 * (tid + 256 * i);
+      if (k0 >= K) continue;
+      f32x4 y = h[i] * inv;
+      if (p.ada_scale) y = y * (1.0f + *reinterpret_cast<const f32x4*>(p.ada_scale + k0));
+      if (p.ada_shift) y = y + *reinterpret_cast<const f32x4*>(p.ada_shift + k0);
+      store_operand4(p.operand, ODT, p.MB, m, k0, y.x, y.y, y.z, y.w, as, false);
+      record_amax(p.amax, y.x, y.y, y.z, y.w);
+    }
+  }
+}
+
+template <int SPL, int G>
+static void launch_odt(const RnqParams& p, dim3 g, dim3 b, hipStream_t s) {
+  if (!p.operand) hipLaunchKernelGGL((rnq_kernel<SPL, G, 0>), g, b, 0, s, p);
+  else if (p.out_dtype == FRT_BF16) hipLaunchKernelGGL((rnq_kernel<SPL, G, FRT_BF16>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((rnq_kernel<SPL, G, FRT_E4M3>), g, b, 0, s, p);
+}
+
+template <int SPL>
+static void launch_g(const RnqParams& p, dim3 g, dim3 b, hipStream_t s) {
+  switch ((p.K + 1023) / 1024) {
+    case 1: launch_odt<SPL, 1>(p, g, b, s); break;
+    case 2: launch_odt<SPL, 2>(p, g, b, s); break;
+    case 3: launch_odt<SPL, 3>(p, g, b, s); break;
+    default: launch_odt<SPL, 4>(p, g, b, s); break;
   }
 }
 
 hipError_t launch_rnq(const RnqParams& p, hipStream_t s) {
   const int rows = p.operand ? p.MB * 16 : p.M;
   const dim3 g(rows), b(256);
-  const int sp = p.x ? p.x_splits : 0;
-  if (sp == 0) hipLaunchKernelGGL(rnq_kernel<0>, g, b, 0, s, p);
-  else if (sp == 1) hipLaunchKernelGGL(rnq_kernel<1>, g, b, 0, s, p);
-  else if (sp == 2) hipLaunchKernelGGL(rnq_kernel<2>, g, b, 0, s, p);
-  else if (sp <= 4) hipLaunchKernelGGL(rnq_kernel<4>, g, b, 0, s, p);
-  else if (sp <= 8) hipLaunchKernelGGL(rnq_kernel<8>, g, b, 0, s, p);
-  else hipLaunchKernelGGL(rnq_kernel<16>, g, b, 0, s, p);
+  switch (p.x ? p.x_splits : 0) {
+    case 0: launch_g<0>(p, g, b, s); break;
+    case 1: launch_g<1>(p, g, b, s); break;
+    case 2: launch_g<2>(p, g, b, s); break;
+    case 4: launch_g<4>(p, g, b, s); break;
+    case 8: launch_g<8>(p, g, b, s); break;
+    default: launch_g<-1>(p, g, b, s); break;
+  }
   return hipGetLastError();
 }
 
