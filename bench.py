@@ -53,36 +53,31 @@ def time_chain(torch, ch, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per decision
 
 
-def time_dominant_gemm(torch, frt, device, synth, dims, dtype, reps=128):
-    """The gate|up GEMM of one layer (M x hidden x 2*mlp, SiLU-gate epilogue) timed alone.
+def time_gemm(torch, frt, device, synth, M, K, N, dtype, reps=128, pool_bytes=1 << 30):
+    """One gate|up GEMM (M x K x N, SiLU-gate epilogue, the library's split) timed alone.
 
     A pool of distinct packed weight copies (>= 1 GiB, 4x the last-level cache) is cycled
     so every launch streams its weights from HBM; the launches replay as one graph, the
-    same way the chain issues them.  Returns (mean us per launch, bytes, splits).
+    same way the chain issues them, and HIP events on that stream bracket the replay.
+    Returns (mean us per launch, algorithmic bytes per launch, splits).
     """
-    M, H, F = dims["M"], dims["hidden"], dims["mlp"]
-    N = 2 * F
-    w = synth.weight_bf16(synth.TEST_SEED, 6, 0, H, N)
+    w = synth.weight_bf16(synth.TEST_SEED, 6, 0, K, N)
     pk, cs = device.pack_weight(w, dtype, frt.W_GATE_UP)
     wbytes = pk.numel()
-    ncopy = max(8, int((1 << 30) // wbytes) + 1)
+    ncopy = max(8, int(pool_bytes // wbytes) + 1)
     pool = [pk.clone() for _ in range(ncopy)]
-    a = device.empty_bytes(frt.frt_operand_bytes(dtype, M, H))
+    a = device.empty_bytes(frt.frt_operand_bytes(dtype, M, K))
     a.zero_()
-    out = device.empty_bytes(frt.frt_operand_bytes(dtype, M, F))
-    splits = 1  # the chain's choice for a GEMM that ends in an epilogue
-    parts = None
+    out = device.empty_bytes(frt.frt_operand_bytes(dtype, M, N // 2))
+    splits = 1  # the library's choice for a GEMM that ends in an epilogue
     stream = torch.cuda.current_stream()
 
     def launch(i, st):
-        frt.frt_skinny_gemm_splitk(M, N, H, splits, dtype, frt.W_GATE_UP, a, pool[i % ncopy], cs, 1.0,
-                                   parts, 0 if parts is None else parts.numel() * 4, frt.EPI_SILU_GATE_QUANT,
-                                   out, dtype, 1.0, stream=st)
+        frt.frt_skinny_gemm_splitk(M, N, K, splits, dtype, frt.W_GATE_UP, a, pool[i % ncopy], cs, 1.0,
+                                   None, 0, frt.EPI_SILU_GATE_QUANT, out, dtype, 1.0, stream=st)
     for i in range(ncopy):
         launch(i, stream.cuda_stream)
     torch.cuda.synchronize()
-    # capture the launches into one graph (as the chain runs them) so host launch gaps
-    # do not count; each replay cycles through the whole cold pool
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         cap = torch.cuda.current_stream().cuda_stream
@@ -98,11 +93,38 @@ def time_dominant_gemm(torch, frt, device, synth, dims, dtype, reps=128):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
     extra = (N * 4) if cs is not None else 0
+    del pool, graph
+    torch.cuda.empty_cache()
     return us, wbytes + extra, splits
 
 
+def time_dominant_gemm(torch, frt, device, synth, dims, dtype, reps=128):
+    """The gate|up GEMM of one action-decoder layer (M x hidden x 2*mlp)."""
+    return time_gemm(torch, frt, device, synth, dims["M"], dims["hidden"], 2 * dims["mlp"], dtype, reps)
+
+
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}  # MI355X dense, published
+
+
+def gemm_sweep(torch, frt, device, synth):
+    """Gate|up GEMM K=2048, N=16384 over M in {1,10,16,32,50,64}, bf16 and e4m3: the
+    roofline curve (achieved HBM GB/s on weight streaming, MFMA utilisation)."""
+    K, N = 2048, 16384
+    rows = []
+    for name, dt in (("bf16", frt.BF16), ("e4m3", frt.E4M3)):
+        for M in (1, 10, 16, 32, 50, 64):
+            us, nbytes, s = time_gemm(torch, frt, device, synth, M, K, N, dt, reps=64)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            util = 2.0 * M * K * N / (us * 1e-6) / (MFMA_PEAK_TFLOPS[name] * 1e12)
+            rows.append(dict(M=M, dtype=name, splits=s, us=round(us, 3), gbs=round(gbs, 1),
+                             hbm_frac=round(gbs / HBM_PEAK_GBS, 4), mfma_util=round(util, 5)))
+            log(f"sweep K={K} N={N} M={M} {name}: {us:.2f} us, {gbs:.0f} GB/s, MFMA {util:.2%}")
+    return rows
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gate_up_gemm_bf16_m50_hbm_traffic.md")
-GEMM_SOURCES = [os.path.join(ROOT, "gemm_chains_amd", "csrc", f) for f in ("gemm.hip", "frt_internal.hpp")]
+GEMM_SOURCES = [os.path.join(ROOT, "gemm_chains_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm_kernel.hpp", "gemm_bf16.hip", "frt_internal.hpp")]
 
 
 def measured_traffic():
@@ -241,6 +263,8 @@ def main():
     log(f"dominant kernel (gate|up GEMM {dims50['M']}x{dims50['hidden']}x{2 * dims50['mlp']}, s={splits}): "
         f"{us:.2f} us, {achieved:.0f} GB/s")
 
+    sweep = gemm_sweep(torch, frt, device, synth)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample")
@@ -279,6 +303,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": f"skinny_gemm gate|up {dims50['M']}x{dims50['hidden']}x{2 * dims50['mlp']} "
                                f"bf16 s={splits} +SiLU epilogue", "us_per_launch": round(us, 3)},
+        "mfma_util_dominant": round(2.0 * dims50["M"] * dims50["hidden"] * 2 * dims50["mlp"] / (us * 1e-6)
+                                    / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), 5),
+        "gemm_sweep_k2048_n16384": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

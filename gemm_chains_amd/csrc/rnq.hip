@@ -133,6 +133,7 @@ hipError_t launch_rnq(const RnqParams& p, hipStream_t s) {
     case 2: launch_g<2>(p, g, b, s); break;
     case 4: launch_g<4>(p, g, b, s); break;
     case 8: launch_g<8>(p, g, b, s); break;
+    case 16: launch_g<16>(p, g, b, s); break;
     default: launch_g<-1>(p, g, b, s); break;
   }
   return hipGetLastError();
