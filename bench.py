@@ -221,7 +221,7 @@ def main():
         nl = dims["layers"] * dims["steps"]
         packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
         variants = [("bf16", False), ("bf16", True)] if M == 50 else [("bf16", False)]
-        for dt_name, pf in variants:  # M=50: paired ablation of the weight-prefetch branch
+        for dt_name, pf in variants:  # M=50: paired ablation of the weight read-ahead
             ch = chain.Chain(dims, packed, use_graph=True, prefetch_next=pf)
             chain.load_workload(ch, wl)
             torch.cuda.synchronize()
@@ -287,8 +287,8 @@ def main():
         "config": {"workload": "action-decoder chain, 18 layers x 10 flow steps, M=50, hidden 1024, "
                                "8 q heads / 1 kv head x 128, 800-token prefix, MLP 4096, bf16, hipGraph replay",
                    "layers": dims50["layers"], "flow_steps": dims50["steps"], "M": 50,
-                   "kernels_per_decision": r["kernels"], "weight_prefetch_branch": best_pf},
-        "ablation_prefetch": {"us_per_layer_m50_off": round(results[(50, "bf16", False)]["us_layer"], 3),
+                   "kernels_per_decision": r["kernels"], "weight_read_ahead": best_pf},
+        "ablation_weight_read_ahead": {"us_per_layer_m50_off": round(results[(50, "bf16", False)]["us_layer"], 3),
                               "us_per_layer_m50_on": round(results[(50, "bf16", True)]["us_layer"], 3)},
         "e4m3": {"us_per_layer_m50": round(results[(50, "e4m3", False)]["us_layer"], 3),
                  "us_per_layer_m10": round(results[(10, "e4m3", False)]["us_layer"], 3),

@@ -20,31 +20,6 @@ namespace frt {
 
 enum { SITE_QKV = 0, SITE_O = 1, SITE_UP = 2, SITE_DOWN = 3 };
 
-// Reads a layer's four packed weights (and nothing else) so that they sit in the
-// last-level cache when the layer's GEMMs stream them.  Runs on a concurrent graph
-// branch with a small grid; the loaded data is folded into a value that is never stored.
-struct PrefetchParams {
-  const u32x4* w[4];
-  size_t n16[4];  // 16-byte units
-  unsigned* sink;
-};
-__global__ void __launch_bounds__(256) prefetch_kernel(const PrefetchParams p) {
-  unsigned acc = 0;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const u32x4* w = p.w[m];
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.n16[m]; i += 4 * stride) {
-      u32x4 a = w[i];
-      u32x4 b = i + stride < p.n16[m] ? w[i + stride] : a;
-      u32x4 c = i + 2 * stride < p.n16[m] ? w[i + 2 * stride] : a;
-      u32x4 d = i + 3 * stride < p.n16[m] ? w[i + 3 * stride] : a;
-      acc ^= a.x ^ b.y ^ c.z ^ d.w;
-    }
-  }
-  if (acc == 0x9e3779b9u && p.sink) *p.sink = acc;  // keeps the loads; practically never taken
-}
-constexpr int kPrefetchBlocks = 64;
 enum { MOD_SCALE = 0, MOD_SHIFT = 1, MOD_GATE = 2 };
 
 struct Buf {
@@ -187,28 +162,13 @@ static uint8_t* at(frt_chain* c, const Buf& b, size_t idx = 0, size_t stride = 0
 }
 
 // Enqueue the whole chain on `s` (eager launches; also what graph capture records).
-static int enqueue_prefetch(frt_chain* c, int l, hipStream_t side) {
-  const frt_chain_desc& d = c->d;
-  const int ks = d.dtype == FRT_BF16 ? 2 : 1;
-  const int H = d.hidden, F = d.mlp, nq = d.n_heads * d.head_dim, nqkv = nq + 2 * d.head_dim;
-  PrefetchParams p{};
-  const void* w[4] = {c->wq[l], c->wo[l], c->wu[l], c->wd[l]};
-  const size_t bytes[4] = {(size_t)H * nqkv * ks, (size_t)nq * H * ks, (size_t)H * 2 * F * ks, (size_t)F * H * ks};
-  for (int i = 0; i < 4; ++i) {
-    p.w[i] = (const u32x4*)w[i];
-    p.n16[i] = bytes[i] / 16;
-  }
-  p.sink = (unsigned*)at(c, c->L.sink);
-  hipLaunchKernelGGL(prefetch_kernel, dim3(kPrefetchBlocks), dim3(256), 0, side, p);
-  FRT_HIP(hipGetLastError());
-  return FRT_OK;
-}
-
-// side / fork / join: when given (graph capture with prefetch_next), layer l's first
-// kernel is followed by an event that a side stream waits on before reading the weights
-// of the layer after l; the side stream rejoins the main stream at the end.
-static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, hipStream_t side = nullptr,
-                         hipEvent_t* evs = nullptr, unsigned* amax = nullptr) {
+// With prefetch_next, the producer before the gate|up GEMM reads the down projection's
+// weights ahead from extra workgroups on the XCDs that will stream them (the launch-
+// overlap analogue); the down GEMM then finds them in L2.  Measured on MI355X, this is
+// the one placement that pays: reading the QKV/O weights in the first producer, or the
+// gate|up weights in the attention kernels or the second producer, slowed the chain
+// (the extra traffic delays those kernels' own loads more than the GEMMs gain).
+static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax = nullptr) {
   const frt_chain_desc& d = c->d;
   const ChainLayout& L = c->L;
   const int M = d.M, H = d.hidden, F = d.mlp, MB = m_blocks(M);
@@ -220,6 +180,10 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, hipStream_t si
   auto modp = [&](int k, int l, int sub, int row) { return mod + (((size_t)k * d.layers + l) * 2 + sub) * modsz + (size_t)row * H; };
   auto actp = [&](int l, int site) -> const float* { return e4 ? act + l * 4 + site : nullptr; };
   int n = 0;
+  const bool pf = d.prefetch_next != 0;
+  unsigned* sink = (unsigned*)at(c, L.sink);
+  const int rows = MB * 16;
+  const int touch_wgs = ((256 - rows) / 8) * 8;  // fill the remaining CUs
 
   const float* h_prev = (const float*)at(c, L.x_in);
   const float* pdown_prev = nullptr;
@@ -240,6 +204,38 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, hipStream_t si
       uint16_t* kcl = (uint16_t*)at(c, L.kc) + (size_t)l * L.kv_len * d.head_dim;
       uint16_t* vcl = (uint16_t*)at(c, L.vc) + (size_t)l * d.head_dim * L.ldv;
 
+      // the layer's four GEMMs
+      GemmParams gq{};
+      gq.M = M; gq.MB = MB; gq.ab_dtype = d.dtype; gq.layout = FRT_W_PLAIN;
+      gq.N = L.nqkv; gq.K = H; gq.splits = L.s_qkv; gq.ksteps_per_split = H / kstep_of(d.dtype) / L.s_qkv;
+      gq.a = a_qkv; gq.w = (const uint8_t*)c->wq[l]; gq.colscale = e4 ? c->sq[l] : nullptr;
+      gq.act_scale = 1.f; gq.act_scale_ptr = actp(l, SITE_QKV); gq.partials = p_qkv; gq.epi = kEpiQkv;
+      gq.q_out = qbuf; gq.k_out = kcl + (size_t)d.prefix_len * d.head_dim;
+      gq.v_out = vcl + d.prefix_len; gq.v_ld = L.ldv; gq.nq = L.nattn; gq.hd = d.head_dim;
+
+      GemmParams go = gq;
+      go.N = H; go.K = L.nattn; go.splits = L.s_o; go.ksteps_per_split = L.nattn / kstep_of(d.dtype) / L.s_o;
+      go.a = a_o; go.w = (const uint8_t*)c->wo[l]; go.colscale = e4 ? c->so[l] : nullptr;
+      go.act_scale_ptr = actp(l, SITE_O); go.partials = p_o; go.epi = FRT_EPI_NONE; go.amax = nullptr;
+
+      GemmParams gu = go;
+      gu.N = 2 * F; gu.K = H; gu.splits = L.s_up; gu.ksteps_per_split = H / kstep_of(d.dtype) / L.s_up;
+      gu.layout = FRT_W_GATE_UP; gu.a = a_up; gu.w = (const uint8_t*)c->wu[l]; gu.colscale = e4 ? c->su[l] : nullptr;
+      gu.act_scale_ptr = actp(l, SITE_UP);
+      gu.out_dtype = d.dtype; gu.out_scale = 1.f; gu.out_scale_ptr = actp(l, SITE_DOWN);
+      gu.amax = amax ? amax + l * 4 + SITE_DOWN : nullptr;
+      if (L.s_up == 1) {
+        gu.epi = FRT_EPI_SILU_GATE_QUANT; gu.out = a_down; gu.partials = nullptr;
+      } else {
+        gu.epi = FRT_EPI_NONE; gu.partials = (float*)at(c, L.p_up);
+      }
+
+      GemmParams gd = gu;
+      gd.N = H; gd.K = F; gd.splits = L.s_down; gd.ksteps_per_split = F / kstep_of(d.dtype) / L.s_down;
+      gd.layout = FRT_W_PLAIN; gd.a = a_down; gd.w = (const uint8_t*)c->wd[l]; gd.colscale = e4 ? c->sd[l] : nullptr;
+      gd.act_scale_ptr = actp(l, SITE_DOWN); gd.epi = FRT_EPI_NONE; gd.partials = p_down; gd.out = nullptr;
+      gd.amax = nullptr;
+
       // 1. producer: add the previous layer's MLP output, AdaRMSNorm (attention sublayer)
       RnqParams a{};
       a.M = M; a.K = H; a.MB = MB;
@@ -252,32 +248,16 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, hipStream_t si
       a.eps = d.eps; a.out_dtype = d.dtype; a.act_scale = 1.f; a.act_scale_ptr = actp(l, SITE_QKV);
       a.operand = a_qkv;
       a.amax = amax ? amax + l * 4 + SITE_QKV : nullptr;
+      a.sink = sink;
       FRT_HIP(launch_rnq(a, s)); ++n;
-      if (side) {  // prefetch the next layer in chain order while this one runs
-        const int idx_next = k * d.layers + l + 1;
-        if (idx_next < d.steps * d.layers) {
-          FRT_HIP(hipEventRecord(evs[idx_next], s));
-          FRT_HIP(hipStreamWaitEvent(side, evs[idx_next], 0));
-          int rc = enqueue_prefetch(c, idx_next % d.layers, side);
-          if (rc != FRT_OK) return rc;
-          ++n;
-        }
-      }
 
       // 2. fused QKV GEMM: bf16 Q into its buffer, own K/V rows after the cached prefix
-      GemmParams g{};
-      g.M = M; g.MB = MB; g.ab_dtype = d.dtype; g.layout = FRT_W_PLAIN;
-      g.N = L.nqkv; g.K = H; g.splits = L.s_qkv; g.ksteps_per_split = H / kstep_of(d.dtype) / L.s_qkv;
-      g.a = a_qkv; g.w = (const uint8_t*)c->wq[l]; g.colscale = e4 ? c->sq[l] : nullptr;
-      g.act_scale = 1.f; g.act_scale_ptr = actp(l, SITE_QKV); g.partials = p_qkv; g.epi = kEpiQkv;
-      g.q_out = qbuf; g.k_out = kcl + (size_t)d.prefix_len * d.head_dim;
-      g.v_out = vcl + d.prefix_len; g.v_ld = L.ldv; g.nq = L.nattn; g.hd = d.head_dim;
-      FRT_HIP(launch_gemm(g, s)); ++n;
+      FRT_HIP(launch_gemm(gq, s)); ++n;
       if (L.s_qkv > 1) {
         ReduceParams r{};
         r.M = M; r.N = L.nqkv; r.MB = MB; r.splits = L.s_qkv; r.partials = p_qkv;
-        r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_QKV); r.colscale = g.colscale; r.epi = kEpiQkv;
-        r.q_out = g.q_out; r.k_out = g.k_out; r.v_out = g.v_out; r.nq = g.nq; r.hd = g.hd; r.v_ld = g.v_ld;
+        r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_QKV); r.colscale = gq.colscale; r.epi = kEpiQkv;
+        r.q_out = gq.q_out; r.k_out = gq.k_out; r.v_out = gq.v_out; r.nq = gq.nq; r.hd = gq.hd; r.v_ld = gq.v_ld;
         FRT_HIP(launch_reduce(r, s)); ++n;
       }
 
@@ -291,10 +271,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, hipStream_t si
       FRT_HIP(launch_attention(t, s)); n += attention_kernel_count(L.kv_len);
 
       // 4. O projection -> partials
-      g.N = H; g.K = L.nattn; g.splits = L.s_o; g.ksteps_per_split = L.nattn / kstep_of(d.dtype) / L.s_o;
-      g.a = a_o; g.w = (const uint8_t*)c->wo[l]; g.colscale = e4 ? c->so[l] : nullptr;
-      g.act_scale_ptr = actp(l, SITE_O); g.partials = p_o; g.epi = FRT_EPI_NONE; g.amax = nullptr;
-      FRT_HIP(launch_gemm(g, s)); ++n;
+      FRT_HIP(launch_gemm(go, s)); ++n;
 
       // 5. producer: gated residual of the attention output, AdaRMSNorm (MLP sublayer)
       RnqParams b = a;
@@ -304,34 +281,25 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, hipStream_t si
       b.ada_scale = modp(k, l, 1, MOD_SCALE); b.ada_shift = modp(k, l, 1, MOD_SHIFT);
       b.act_scale_ptr = actp(l, SITE_UP); b.operand = a_up;
       b.amax = amax ? amax + l * 4 + SITE_UP : nullptr;
+      if (pf) {
+        b.touch[0] = gemm_weight_touch(gd, 0, 1);
+        b.touch_wgs = touch_wgs;
+      }
       FRT_HIP(launch_rnq(b, s)); ++n;
 
       // 6. gate|up GEMM with SiLU(gate)*up + quantise (fused when not split)
-      g.N = 2 * F; g.K = H; g.splits = L.s_up; g.ksteps_per_split = H / kstep_of(d.dtype) / L.s_up;
-      g.layout = FRT_W_GATE_UP; g.a = a_up; g.w = (const uint8_t*)c->wu[l]; g.colscale = e4 ? c->su[l] : nullptr;
-      g.act_scale_ptr = actp(l, SITE_UP);
-      g.out_dtype = d.dtype; g.out_scale = 1.f; g.out_scale_ptr = actp(l, SITE_DOWN);
-      g.amax = amax ? amax + l * 4 + SITE_DOWN : nullptr;
-      if (L.s_up == 1) {
-        g.epi = FRT_EPI_SILU_GATE_QUANT; g.out = a_down; g.partials = nullptr;
-        FRT_HIP(launch_gemm(g, s)); ++n;
-      } else {
-        g.epi = FRT_EPI_NONE; g.partials = (float*)at(c, L.p_up);
-        FRT_HIP(launch_gemm(g, s)); ++n;
+      FRT_HIP(launch_gemm(gu, s)); ++n;
+      if (L.s_up > 1) {
         ReduceParams r{};
-        r.M = M; r.N = 2 * F; r.MB = MB; r.splits = L.s_up; r.partials = g.partials;
-        r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_UP); r.colscale = g.colscale;
+        r.M = M; r.N = 2 * F; r.MB = MB; r.splits = L.s_up; r.partials = gu.partials;
+        r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_UP); r.colscale = gu.colscale;
         r.epi = FRT_EPI_SILU_GATE_QUANT; r.out = a_down; r.out_dtype = d.dtype; r.out_scale = 1.f;
-        r.out_scale_ptr = actp(l, SITE_DOWN); r.amax = g.amax;
+        r.out_scale_ptr = actp(l, SITE_DOWN); r.amax = gu.amax;
         FRT_HIP(launch_reduce(r, s)); ++n;
       }
 
       // 7. down projection -> partials, reduced by the next producer
-      g.N = H; g.K = F; g.splits = L.s_down; g.ksteps_per_split = F / kstep_of(d.dtype) / L.s_down;
-      g.layout = FRT_W_PLAIN; g.a = a_down; g.w = (const uint8_t*)c->wd[l]; g.colscale = e4 ? c->sd[l] : nullptr;
-      g.act_scale_ptr = actp(l, SITE_DOWN); g.epi = FRT_EPI_NONE; g.partials = p_down; g.out = nullptr;
-      g.amax = nullptr;
-      FRT_HIP(launch_gemm(g, s)); ++n;
+      FRT_HIP(launch_gemm(gd, s)); ++n;
 
       h_prev = h_mlp;
       pdown_prev = p_down;
@@ -404,38 +372,11 @@ extern "C" int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_de
         (void)hipEventDestroy(ev);
       }
     }
-    // optional concurrent prefetch branch: a side stream and one fork event per layer-step
-    hipStream_t side = nullptr;
-    std::vector<hipEvent_t> evs;
-    hipEvent_t join = nullptr;
-    const int nls = desc->steps * desc->layers;
-    if (desc->prefetch_next) {
-      bool ok = hipStreamCreateWithFlags(&side, hipStreamNonBlocking) == hipSuccess &&
-                hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess;
-      evs.assign(nls, nullptr);
-      for (int i = 0; ok && i < nls; ++i) ok = hipEventCreateWithFlags(&evs[i], hipEventDisableTiming) == hipSuccess;
-      if (!ok) {
-        for (hipEvent_t ev : evs) if (ev) (void)hipEventDestroy(ev);
-        if (join) (void)hipEventDestroy(join);
-        if (side) (void)hipStreamDestroy(side);
-        (void)hipStreamDestroy(cs);
-        delete c;
-        return FRT_E_HIP;
-      }
-    }
     e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     int n = 0;
-    int rc = e == hipSuccess ? enqueue_chain(c, cs, &n, side, side ? evs.data() : nullptr) : FRT_E_HIP;
-    if (side && e == hipSuccess) {  // rejoin the side branch before the capture ends
-      hipError_t ej = hipEventRecord(join, side);
-      if (ej == hipSuccess) ej = hipStreamWaitEvent(cs, join, 0);
-      if (ej != hipSuccess && rc == FRT_OK) { set_hip_error((int)ej); rc = FRT_E_HIP; }
-    }
+    int rc = e == hipSuccess ? enqueue_chain(c, cs, &n) : FRT_E_HIP;
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(cs, &g);
-    for (hipEvent_t ev : evs) (void)hipEventDestroy(ev);
-    if (join) (void)hipEventDestroy(join);
-    if (side) (void)hipStreamDestroy(side);
     if (e != hipSuccess) set_hip_error((int)e);
     if (rc == FRT_OK && e2 != hipSuccess) { set_hip_error((int)e2); rc = FRT_E_HIP; }
     if (rc == FRT_OK) {
@@ -507,7 +448,7 @@ extern "C" int frt_layer_chain_calibrate(frt_chain* c, void* stream, float* scal
   hipStream_t s = (hipStream_t)stream;
   unsigned* amax = (unsigned*)at(c, c->L.amax);
   FRT_HIP(hipMemsetAsync(amax, 0, (size_t)n * 4, s));
-  int rc = enqueue_chain(c, s, nullptr, nullptr, nullptr, amax);
+  int rc = enqueue_chain(c, s, nullptr, amax);
   if (rc != FRT_OK) return rc;
   hipLaunchKernelGGL(amax_to_scale_kernel, dim3((n + 255) / 256), dim3(256), 0, s, (const unsigned*)amax, scales_dev, n);
   FRT_HIP(hipGetLastError());

@@ -211,6 +211,61 @@ __device__ __forceinline__ void store_qkv4(uint16_t* q_out, uint16_t* k_out, uin
   }
 }
 
+// ------------------------------------------------------------------ weight touching
+// The packed weight bytes a following GEMM launch will read, described by that launch's
+// shape, so that a latency-bound kernel can read them ahead from workgroups on the same
+// XCDs as the GEMM workgroups that will stream them (their L2 then serves the GEMM; the
+// memory-side cache serves it otherwise).  Workgroups are dispatched round-robin over the
+// 8 XCDs, so linear workgroup id L runs on XCD L % 8.
+struct WeightTouch {
+  const uint8_t* w;          // null: nothing to touch
+  int tb, ks;                // tile bytes; k-steps of the whole K
+  int nt, kps, col_groups, row_groups, splits;
+  int part, parts;           // touch units u with u % parts == part
+};
+
+// Reads one dword of every 64-byte segment of the GEMM workgroups' weight bytes that
+// belong to this workgroup's XCD, spread over the touching workgroups of that XCD among
+// the `count` with linear ids [first, first + count).  Returns a value the caller folds
+// into a store that never happens, so the loads stay.
+__device__ __forceinline__ unsigned touch_weights(const WeightTouch& t, int L, int first, int count) {
+  if (!t.w) return 0u;
+  const int c = L & 7;
+  const int c0 = (c - (first & 7) + 8) & 7;     // offset of XCD c's first toucher
+  const int i = (L - first - c0) >> 3;           // index among them
+  const int nc = (count - c0 + 7) >> 3;          // how many there are
+  const int per_xcd = t.row_groups > 1 ? ((t.col_groups - c + 7) >> 3) * t.splits
+                                       : (t.col_groups * t.splits - c + 7) >> 3;
+  const int nunits = per_xcd > 0 ? per_xcd : 0;
+  const int nseg = t.kps * t.tb / 64;  // per tile
+  unsigned acc = 0u;
+  for (int u = i; u < nunits; u += nc) {
+    if (u % t.parts != t.part) continue;
+    int g, y;
+    if (t.row_groups > 1) {
+      g = c + 8 * (u / t.splits);
+      y = u % t.splits;
+    } else {
+      const int Lg = c + 8 * u;
+      g = Lg % t.col_groups;
+      y = Lg / t.col_groups;
+    }
+    for (int tt = 0; tt < t.nt; ++tt) {
+      const uint8_t* base = t.w + ((size_t)(g * t.nt + tt) * t.ks + (size_t)y * t.kps) * t.tb;
+      for (int s0 = threadIdx.x; s0 < nseg; s0 += 4 * blockDim.x) {
+        unsigned v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int sg = s0 + q * blockDim.x;
+          v[q] = sg < nseg ? *reinterpret_cast<const unsigned*>(base + (size_t)sg * 64) : 0u;
+        }
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      }
+    }
+  }
+  return acc;
+}
+
 // ------------------------------------------------------------------ kernel parameter blocks
 struct RnqParams {
   int M, K, MB;
@@ -230,6 +285,9 @@ struct RnqParams {
   const float* act_scale_ptr;
   uint8_t* operand;          // packed or null
   unsigned* amax;            // calibration: running max |value before rounding| (float bits), or null
+  WeightTouch touch[2];      // weights of following GEMMs read ahead by extra workgroups
+  int touch_wgs;             // extra workgroups after the rows (a multiple of 8), or 0
+  unsigned* sink;            // never written in practice (keeps the touch loads)
 };
 
 struct GemmParams {
@@ -299,6 +357,8 @@ int attention_kernel_count(int kv_len);
 // Launchers (stream-ordered, no validation: callers validate first).
 hipError_t launch_rnq(const RnqParams& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+// What launch_gemm(p) will read of p.w, as touch units; split into `parts` parts.
+WeightTouch gemm_weight_touch(const GemmParams& p, int part, int parts);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 // Library choices of split count and waves per workgroup.

@@ -121,6 +121,22 @@ static GemmShape choose_shape(const GemmParams& p) {
   return sh;
 }
 
+WeightTouch gemm_weight_touch(const GemmParams& p, int part, int parts) {
+  const GemmShape sh = choose_shape(p);
+  WeightTouch t{};
+  t.w = p.w;
+  t.tb = p.ab_dtype == FRT_BF16 ? 1024 : 2048;
+  t.ks = p.K / kstep_of(p.ab_dtype);
+  t.nt = sh.nt;
+  t.kps = p.ksteps_per_split;
+  t.col_groups = sh.col_groups;
+  t.row_groups = sh.row_groups;
+  t.splits = p.splits;
+  t.part = part;
+  t.parts = parts;
+  return t;
+}
+
 hipError_t launch_gemm(const GemmParams& p_in, hipStream_t s) {
   GemmParams p = p_in;
   const GemmShape sh = choose_shape(p);

@@ -33,6 +33,12 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int K = p.K;
   __shared__ float wsum[4];
+  const int rows = p.operand ? p.MB * 16 : p.M;
+  if (m >= rows) {  // extra workgroups: read the following GEMMs' weights ahead
+    const unsigned v = touch_weights(p.touch[0], m, rows, p.touch_wgs) ^ touch_weights(p.touch[1], m, rows, p.touch_wgs);
+    if (v == 0x9e3779b9u && p.sink) *p.sink = v;  // practically never taken
+    return;
+  }
   if (m >= p.M) {  // padding rows of the operand: zero codes (only launched with an operand)
     if constexpr (ODT != 0) {
 #pragma unroll
@@ -126,7 +132,7 @@ static void launch_g(const RnqParams& p, dim3 g, dim3 b, hipStream_t s) {
 
 hipError_t launch_rnq(const RnqParams& p, hipStream_t s) {
   const int rows = p.operand ? p.MB * 16 : p.M;
-  const dim3 g(rows), b(256);
+  const dim3 g(rows + p.touch_wgs), b(256);
   switch (p.x ? p.x_splits : 0) {
     case 0: launch_g<0>(p, g, b, s); break;
     case 1: launch_g<1>(p, g, b, s); break;

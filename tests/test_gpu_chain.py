@@ -121,8 +121,8 @@ def test_chain_parity(F, dtype, M, splits):
     ce.close()
 
 
-def test_prefetch_branch_leaves_results_bit_identical(F):
-    """The concurrent weight-prefetch branch only reads; outputs must not change."""
+def test_weight_read_ahead_leaves_results_bit_identical(F):
+    """Reading the down weights ahead (prefetch_next) only reads; outputs must not change."""
     frt, chain = F
     dims = synth.chain_dims(layers=3, steps=2, M=50)
     wl = synth.workload4(dims)
