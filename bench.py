@@ -103,6 +103,65 @@ def time_dominant_gemm(torch, frt, device, synth, dims, dtype, reps=128):
     return time_gemm(torch, frt, device, synth, dims["M"], dims["hidden"], 2 * dims["mlp"], dtype, reps)
 
 
+def state_reuse(torch, chain, synth, dims, packed, wl, reps=20):
+    """Execution-state capsule and selective refresh on the M=50 bf16 chain.
+
+    Device copies are timed with HIP events on the current stream; the rebuild and the
+    uploads include host work (graph capture, host-to-device copies from NumPy) and are
+    timed on the host clock, each finished by a synchronisation.
+    """
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    a = chain.Chain(dims, packed, use_graph=True)
+    chain.load_workload(a, wl)
+    a.run(stream.cuda_stream)
+    torch.cuda.synchronize()
+    cap = a.snapshot()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us
+
+    snap_us = timed(lambda: a.snapshot(cap, stream.cuda_stream))
+    rest_us = timed(lambda: a.restore(cap, stream.cuda_stream))
+    rest_dec_us = timed(lambda: (a.restore(cap, stream.cuda_stream), a.run(stream.cuda_stream)))
+    dec_us = timed(lambda: a.run(stream.cuda_stream))
+
+    def wall(fn, n=3):
+        best = 1e30
+        for _ in range(n):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            best = min(best, time.perf_counter() - t0)
+        return best * 1e6  # us
+
+    def rebuild():
+        b = chain.Chain(dims, packed, use_graph=True)
+        chain.load_workload(b, wl)
+        b.run(stream.cuda_stream)
+        torch.cuda.synchronize()
+        b.close()
+
+    x_new, _ = synth.chain_inputs(dims, seed=2)
+    full_us = wall(lambda: (chain.load_workload(a, wl), a.run(stream.cuda_stream)))
+    x_only_us = wall(lambda: (a.write("x_in", x_new), a.run(stream.cuda_stream)))
+    rebuild_us = wall(rebuild, n=2)
+    a.close()
+    return dict(state_bytes=int(cap.numel()), snapshot_us=round(snap_us, 2), restore_us=round(rest_us, 2),
+                decision_us=round(dec_us, 1), restore_plus_decision_us=round(rest_dec_us, 1),
+                rebuild_plus_decision_us=round(rebuild_us, 1),
+                full_state_upload_plus_decision_us=round(full_us, 1),
+                x_in_refresh_plus_decision_us=round(x_only_us, 1))
+
+
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}  # MI355X dense, published
 
 
@@ -221,6 +280,9 @@ def main():
         nl = dims["layers"] * dims["steps"]
         packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
         variants = [("bf16", False), ("bf16", True)] if M == 50 else [("bf16", False)]
+        if M == 50:
+            reuse = state_reuse(torch, chain, synth, dims, packed, wl)
+            log(f"state reuse: {reuse}")
         for dt_name, pf in variants:  # M=50: paired ablation of the weight read-ahead
             ch = chain.Chain(dims, packed, use_graph=True, prefetch_next=pf)
             chain.load_workload(ch, wl)
@@ -306,6 +368,7 @@ def main():
         "mfma_util_dominant": round(2.0 * dims50["M"] * dims50["hidden"] * 2 * dims50["mlp"] / (us * 1e-6)
                                     / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), 5),
         "gemm_sweep_k2048_n16384": sweep,
+        "state_reuse_m50_bf16": reuse,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

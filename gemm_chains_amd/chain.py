@@ -80,6 +80,21 @@ class Chain:
     def kernel_count(self):
         return frt.frt_layer_chain_kernel_count(self.handle)
 
+    def state_bytes(self):
+        return frt.frt_layer_chain_state_bytes(self.handle)
+
+    def snapshot(self, capsule=None, stream=None):
+        """Copy the persistent state into a capsule (a uint8 CUDA tensor; new if None)."""
+        n = self.state_bytes()
+        if capsule is None:
+            capsule = device.empty_bytes(n)
+        frt.frt_layer_chain_snapshot(self.handle, capsule, capsule.numel(), stream)
+        return capsule
+
+    def restore(self, capsule, stream=None):
+        """Copy a capsule back into this chain's persistent state (fixed addresses)."""
+        frt.frt_layer_chain_restore(self.handle, capsule, capsule.numel(), stream)
+
     def close(self):
         if self.handle is not None:
             frt.frt_layer_chain_destroy(self.handle)

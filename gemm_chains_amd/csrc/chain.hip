@@ -433,6 +433,30 @@ extern "C" int frt_layer_chain_run(frt_chain* c, void* stream) {
 
 extern "C" int frt_layer_chain_kernel_count(const frt_chain* c) { return c ? c->kernels : -1; }
 
+// The persistent state is the arena's leading region, up to the first working buffer.
+extern "C" size_t frt_layer_chain_state_bytes(const frt_chain* c) { return c ? c->L.h.off : 0; }
+
+static int state_copy(frt_chain* c, void* stream, void* dst, const void* src, const void* capsule, size_t bytes) {
+  FRT_CHECK(c, FRT_E_STATE);
+  FRT_CHECK(capsule, FRT_E_NULL);
+  FRT_CHECK(aligned16(capsule), FRT_E_ALIGN);
+  const size_t n = c->L.h.off;
+  FRT_CHECK(bytes >= n, FRT_E_WORKSPACE);
+  FRT_CHECK(!overlaps(capsule, n, c->arena, c->arena_bytes), FRT_E_ALIAS);
+  FRT_HIP(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+  return FRT_OK;
+}
+
+extern "C" int frt_layer_chain_snapshot(frt_chain* c, void* stream, void* capsule_dev, size_t capsule_bytes) {
+  if (!c) return FRT_E_STATE;
+  return state_copy(c, stream, capsule_dev, c->arena, capsule_dev, capsule_bytes);
+}
+
+extern "C" int frt_layer_chain_restore(frt_chain* c, void* stream, const void* capsule_dev, size_t capsule_bytes) {
+  if (!c) return FRT_E_STATE;
+  return state_copy(c, stream, c->arena, capsule_dev, capsule_dev, capsule_bytes);
+}
+
 __global__ void amax_to_scale_kernel(const unsigned* amax, float* scales, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) scales[i] = __builtin_bit_cast(float, amax[i]) / 448.0f;

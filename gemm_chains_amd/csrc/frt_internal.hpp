@@ -294,8 +294,11 @@ struct GemmParams {
   int M, N, K, MB, splits;
   int ab_dtype, layout;
   int ksteps_per_split;      // K / kstep / splits
-  int kwaves;                // waves per workgroup splitting the chunk (set at launch)
-  int row_groups, col_groups;  // workgroup grid per split (set at launch)
+  // set at launch from the tile shape (so the kernel does no integer division):
+  int kwaves;                // waves per workgroup splitting the chunk
+  int run;                   // k-steps per wave (ksteps_per_split / kwaves)
+  int ksteps;                // k-steps of the whole K
+  int row_groups, col_groups;  // workgroup grid per split
   const uint8_t* a;
   const uint8_t* w;
   const float* colscale;

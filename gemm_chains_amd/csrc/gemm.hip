@@ -141,6 +141,8 @@ hipError_t launch_gemm(const GemmParams& p_in, hipStream_t s) {
   GemmParams p = p_in;
   const GemmShape sh = choose_shape(p);
   p.kwaves = sh.kw;
+  p.run = p.ksteps_per_split / sh.kw;
+  p.ksteps = p.K / kstep_of(p.ab_dtype);
   p.row_groups = sh.row_groups;
   p.col_groups = sh.col_groups;
   return p.ab_dtype == FRT_BF16 ? launch_gemm_typed<FRT_BF16>(p, sh, s) : launch_gemm_typed<FRT_E4M3>(p, sh, s);

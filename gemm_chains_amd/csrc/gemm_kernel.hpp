@@ -102,20 +102,20 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
   // be a scalar branch, never an EXEC-masked one
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kw = p.kwaves;
-  int g, r;
-  if (p.row_groups == 1) {
-    g = blockIdx.x;
-    r = 0;
-  } else {
-    const int L = blockIdx.x, R = p.row_groups;
-    g = (L / (8 * R)) * 8 + (L & 7);
-    r = (L >> 3) % R;
-    if (g >= p.col_groups) return;  // padding of the XCD-aware grid (whole workgroup)
-  }
+  const int KS = p.ksteps;
+  const int run = p.run;  // = PER * rounds
+  // grid: (col_groups, 1, splits), or with row groups (8 * row_groups, ceil(col_groups / 8),
+  // splits), where x = 8 r + g % 8 and y = g / 8: linear id = g % 8 (mod 8), so all row
+  // groups of a column group run on its XCD
+  const int g_grid = p.row_groups == 1 ? (int)blockIdx.x : (int)(blockIdx.y * 8 + (blockIdx.x & 7));
+  const int r = p.row_groups == 1 ? 0 : (int)(blockIdx.x >> 3);
+  // padding workgroups of the row-group grid repeat the last column group's loads (in
+  // bounds) and store nothing: no branch ahead of the loads, so every kernel argument is
+  // fetched in one batch
+  const bool active = g_grid < p.col_groups;
+  const int g = active ? g_grid : p.col_groups - 1;
   const int mb0 = r * MB;  // first 16-row block of this workgroup
-  const int split = blockIdx.y;
-  const int KS = p.K / (DT == FRT_BF16 ? 32 : 128);
-  const int run = p.ksteps_per_split / kw;  // = PER * rounds
+  const int split = blockIdx.z;
   const int ks_begin = split * p.ksteps_per_split + wave * run;
 
   const uint8_t* wbase[NT];
@@ -130,7 +130,8 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int b = 0; b < MB; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks0 = ks_begin; ks0 < ks_begin + run; ks0 += PER) {
+  int ks0 = ks_begin;
+  do {  // run = PER * rounds, rounds >= 1
     Frag<DT> wf[PER][NT];
     Frag<DT> af[PER][MB];
 #pragma unroll
@@ -147,7 +148,9 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int b = 0; b < MB; ++b) acc[t][b] = mma(wf[u][t], af[u][b], acc[t][b]);
-  }
+    ks0 += PER;
+  } while (ks0 < ks_begin + run);
+  if (!active) return;  // whole workgroup
 
   // ---- epilogue (one per kernel)
   const float as = load_scale(p.act_scale_ptr, p.act_scale);
@@ -225,10 +228,10 @@ static hipError_t launch_t(const GemmParams& p, const GemmShape& sh, hipStream_t
   if constexpr (PER * (NT + MB) * (DT == FRT_BF16 ? 4 : 8) > 192 || (silu && NT % 2)) {
     return hipErrorInvalidValue;  // never chosen (register budget / SiLU pairs): not instantiated
   } else {
-    const int grid_x = sh.row_groups == 1 ? sh.col_groups : (sh.col_groups + 7) / 8 * 8 * sh.row_groups;
+    const dim3 grid = sh.row_groups == 1 ? dim3(sh.col_groups, 1, p.splits)
+                                         : dim3(8 * sh.row_groups, (sh.col_groups + 7) / 8, p.splits);
     const size_t lds = (size_t)p.kwaves * NT * MB * 64 * sizeof(f32x4);
-    hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI>), dim3(grid_x, p.splits), dim3(64 * p.kwaves),
-                       lds, s, p);
+    hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI>), grid, dim3(64 * p.kwaves), lds, s, p);
     return hipGetLastError();
   }
 }

@@ -74,6 +74,9 @@ _SIGS = {
     "frt_layer_chain_run": (_int, [_c_void_p, _c_void_p]),
     "frt_layer_chain_calibrate": (_int, [_c_void_p, _c_void_p, _c_void_p]),
     "frt_layer_chain_kernel_count": (_int, [_c_void_p]),
+    "frt_layer_chain_state_bytes": (_size, [_c_void_p]),
+    "frt_layer_chain_snapshot": (_int, [_c_void_p, _c_void_p, _c_void_p, _size]),
+    "frt_layer_chain_restore": (_int, [_c_void_p, _c_void_p, _c_void_p, _size]),
     "frt_layer_chain_destroy": (_int, [_c_void_p]),
 }
 
@@ -279,6 +282,20 @@ def frt_layer_chain_calibrate(chain, scales, stream=None):
 
 def frt_layer_chain_kernel_count(chain):
     return _lib().frt_layer_chain_kernel_count(chain)
+
+
+def frt_layer_chain_state_bytes(chain):
+    return _lib().frt_layer_chain_state_bytes(chain)
+
+
+def frt_layer_chain_snapshot(chain, capsule, capsule_bytes, stream=None):
+    _check(_lib().frt_layer_chain_snapshot(chain, _stream(stream), _ptr(capsule), capsule_bytes),
+           "frt_layer_chain_snapshot")
+
+
+def frt_layer_chain_restore(chain, capsule, capsule_bytes, stream=None):
+    _check(_lib().frt_layer_chain_restore(chain, _stream(stream), _ptr(capsule), capsule_bytes),
+           "frt_layer_chain_restore")
 
 
 def frt_layer_chain_destroy(chain):

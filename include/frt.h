@@ -286,6 +286,21 @@ int frt_layer_chain_buffer(frt_chain* chain, const char* name, void** dev, size_
  * "x_out" like a run.  FRT_E_DTYPE unless the chain is bf16.                          */
 int frt_layer_chain_calibrate(frt_chain* chain, void* stream, float* scales_dev);
 
+/* Execution-state capsule (abstract page, "execution-state capsule": the state a
+ * decision runs on is captured as a unit that can be restored or forked).  The chain's
+ * persistent state -- "x_in", "x_out", "mod", "act_scale", "k_cache", "v_cache" -- is the
+ * leading region of the arena, so a capsule is one device copy of state_bytes bytes:
+ *   snapshot: chain state -> capsule_dev;  restore: capsule_dev -> chain state.
+ * A capsule restores into any chain created with the same shape fields (layers, steps,
+ * M, hidden, n_heads, head_dim, prefix_len, mlp, dtype); restoring it into a second
+ * chain forks the state (that chain may hold other weights).  The copy is queued on
+ * `stream` (asynchronous); capsule_dev is caller-owned device memory, 16-byte aligned,
+ * >= state_bytes, and must not overlap the arena (FRT_E_ALIAS).  The rest of the arena
+ * (working buffers) is rewritten by every run and is not part of the state.           */
+size_t frt_layer_chain_state_bytes(const frt_chain* chain);
+int frt_layer_chain_snapshot(frt_chain* chain, void* stream, void* capsule_dev, size_t capsule_bytes);
+int frt_layer_chain_restore(frt_chain* chain, void* stream, const void* capsule_dev, size_t capsule_bytes);
+
 /* Run every step and layer once on `stream` (one hipGraphLaunch, or eager launches). */
 int frt_layer_chain_run(frt_chain* chain, void* stream);
 /* Kernels one run launches (graph nodes when captured). */

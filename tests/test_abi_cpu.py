@@ -235,6 +235,9 @@ def test_chain_validation():
     assert lib.frt_layer_chain_calibrate(None, None, None) == frt.E_STATE
     assert lib.frt_layer_chain_destroy(None) == frt.E_STATE
     assert lib.frt_layer_chain_kernel_count(None) == -1
+    assert lib.frt_layer_chain_state_bytes(None) == 0
+    assert lib.frt_layer_chain_snapshot(None, None, FAKE, 1 << 20) == frt.E_STATE
+    assert lib.frt_layer_chain_restore(None, None, FAKE, 1 << 20) == frt.E_STATE
     # keep_intermediates grows the arena by the per-(step, layer) debug buffers
     d.splits_up = 0
     d.keep_intermediates = 1
