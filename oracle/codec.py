@@ -1,4 +1,4 @@
-"""Software number formats for the oracle: float64 <-> bfloat16 and OCP E4M3FN codes.
+"""Software number formats for the oracle: float64 <-> bfloat16, OCP E4M3FN and OCP MXFP4 codes.
 
 TEST INFRASTRUCTURE ONLY.  Nothing outside ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU
@@ -142,6 +142,85 @@ def e4m3_decode(c):
 def e4m3_round(v):
     """Round float64 values to the nearest E4M3FN value (saturating)."""
     return e4m3_decode(e4m3_encode(v))
+
+
+# ---------------------------------------------------------------- OCP MXFP4 (E2M1 elements, E8M0 block scales)
+#
+# The pages run the fused action decoder's weights at 4 bits on their NVIDIA target
+# (the FlashRT-PAI abstract and news summary).  On gfx950 the matrix cores take OCP
+# microscaling formats natively, so the 4-bit weights here are OCP MXFP4 ("OCP
+# Microscaling Formats (MX) Specification" v1.0): blocks of 32 consecutive elements along
+# K share one E8M0 scale X = 2**e (e in [-127, 127], byte e + 127); each element is FP4
+# E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5,
+# 2, 3, 4, 6; no infinities or NaN).  The block exponent is floor(log2(max |v|)) minus the
+# largest element exponent (2), so max |v| / X lies in [4, 8); elements are v / X rounded
+# to nearest, ties to even, saturating at +-6.
+
+FP4_MAX = 6.0
+MX_BLOCK = 32
+
+
+def fp4_encode(v):
+    """float64 array -> FP4 E2M1 codes (uint8, low 4 bits): RNE, saturating to +-6, -0 kept.
+
+    Below 1 the quantum is 0.5 (exponent field 0: q in [0, 2], q == 2 is exactly 1.0);
+    from 1 up, E = floor(log2 a) in [0, 2], quantum 2**(E-1), q = rne(a / quantum) in
+    [2, 4] and q == 4 carries into the exponent; past the largest exponent the code
+    saturates at 6.
+    """
+    v = _as_f64(v)
+    sign = np.signbit(v).astype(np.uint32) << 3
+    a = np.abs(v)
+    out = np.zeros(a.shape, np.uint32)
+    sub = a < 1.0
+    out[sub] = np.rint(a[sub] * 2.0).astype(np.uint32)          # 0, 1 (0.5) or 2 (1.0)
+    nrm = ~sub & (a < 8.0)
+    an = a[nrm]
+    e = _floor_log2(an)
+    q = np.rint(np.ldexp(an, 1 - e))
+    carry = q == 4.0
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 2.0, q)
+    code = ((e + 1) << 1) | (q.astype(np.int64) - 2)
+    out[nrm] = np.minimum(code, 7).astype(np.uint32)             # exponent past 2 -> 6
+    out[~sub & ~nrm] = 7                                        # |v| >= 8 (and inf): 6
+    return (out | sign).astype(np.uint8)
+
+
+def fp4_decode(c):
+    """FP4 E2M1 codes -> float64 values."""
+    c = np.asarray(c).astype(np.int64)
+    s = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    return s * np.where(e == 0, m * 0.5, np.ldexp(1.0 + m / 2.0, e - 1))
+
+
+def mxfp4_encode(w):
+    """MXFP4 along axis 0 (K) of w [K][N] (K a multiple of 32).
+
+    Returns (codes [K][N] uint8 FP4, scale bytes [K/32][N] uint8 E8M0, X [K/32][N] float64).
+    A block whose largest magnitude is 0 gets scale byte 0 and zero codes.
+    """
+    w = _as_f64(w)
+    K, N = w.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = w.reshape(K // MX_BLOCK, MX_BLOCK, N)
+    amax = np.max(np.abs(blocks), axis=1)                        # [K/32][N]
+    nz = amax > 0
+    e = np.where(nz, _floor_log2(np.where(nz, amax, 1.0)) - 2, -127)
+    e = np.clip(e, -127, 127)
+    X = np.ldexp(1.0, e)
+    codes = fp4_encode(blocks / X[:, None, :]).reshape(K, N)     # exact scaling by 2**-e
+    return codes, (e + 127).astype(np.uint8), X
+
+
+def mxfp4_decode(codes, scale_bytes):
+    """MXFP4 codes [K][N] with E8M0 scale bytes [K/32][N] -> float64 values [K][N]."""
+    K, N = codes.shape
+    X = np.ldexp(1.0, np.asarray(scale_bytes).astype(np.int64) - 127)
+    return (fp4_decode(codes).reshape(K // MX_BLOCK, MX_BLOCK, N) * X[:, None, :]).reshape(K, N)
 
 
 # ---------------------------------------------------------------- generic

@@ -37,6 +37,11 @@ Readings taken where the pages are silent (each is listed again in the design no
      shared by every query head, scale 1/sqrt(head_dim), no mask; Q, own K, own V
      are rounded to bf16 before use (they are stored in that format).
   R10 flow steps compose: the residual stream leaving step k enters step k+1.
+  R16 4-bit weights (the pages' 4-bit weight path, on gfx950's microscaling matrix
+      cores): OCP MXFP4 -- 32 consecutive k of a column share an E8M0 scale
+      2**(floor(log2 max|w|) - 2); elements are FP4 E2M1, round to nearest even,
+      saturating at 6; an all-zero block gets scale byte 0.  Activations stay e4m3
+      with their static per-site scales; the block scales replace s_w.
 """
 import numpy as np
 
@@ -154,6 +159,21 @@ def pack_weight_values(w_bf16_values, gamma, dtype):
     safe = np.where(s_w > 0, s_w, 1.0)
     v = np.where(s_w[None, :] > 0, w / safe[None, :], 0.0)
     return codec.e4m3_encode(v), s_w, v
+
+
+def pack_weight_mxfp4(w_bf16_values, gamma=None):
+    """Offline weight preparation for 4-bit weights (OCP MXFP4, reading R16).
+
+    W' = diag(gamma) W (float64), then blocks of 32 consecutive k of each column share an
+    E8M0 scale and the elements are FP4 E2M1 codes (codec.mxfp4_encode).  The GEMM uses
+    the decoded values W'' = code * 2**(scale - 127); no per-column scale remains.
+    Returns (codes [K][N], scale bytes [K/32][N], decoded values [K][N]).
+    """
+    w = _f64(w_bf16_values)
+    if gamma is not None:
+        w = fold_gamma(gamma, w)
+    codes, sb, _ = codec.mxfp4_encode(w)
+    return codes, sb, codec.mxfp4_decode(codes, sb)
 
 
 # ----------------------------------------------------------------- GEMM

@@ -99,6 +99,66 @@ def _e4m3_probe_values():
     return np.concatenate([pts, -pts])
 
 
+def test_fp4_golden_values():
+    rows = _read_golden("fp4_e2m1_values.txt")
+    codes = np.array([c for c, _ in rows])
+    vals = np.array([v for _, v in rows])
+    assert len(rows) == 16
+    assert _same(codec.fp4_decode(codes), vals)
+    assert np.array_equal(codec.fp4_encode(vals), codes.astype(np.uint8))
+
+
+def _fp4_brute(v):
+    """Nearest of the 8 E2M1 magnitudes by exhaustive search; ties to the even code
+    (mantissa bit 0); beyond 6 the largest; the sign is copied."""
+    mags = codec.fp4_decode(np.arange(8))
+    out = []
+    for x in np.asarray(v, float):
+        a = abs(x)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        c = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        out.append(c | (8 if np.signbit(x) else 0))
+    return np.array(out, np.uint8)
+
+
+def test_fp4_encode_matches_brute_force_nearest():
+    mags = codec.fp4_decode(np.arange(8))
+    mids = (mags[1:] + mags[:-1]) / 2
+    g = np.random.default_rng(11)
+    v = np.concatenate([mags, mids, np.nextafter(mids, 0), np.nextafter(mids, 10), [6.5, 7.99, 8.0, 1e9],
+                        g.uniform(0, 9, 20000), g.standard_normal(20000) * 3])
+    v = np.concatenate([v, -v])
+    assert np.array_equal(codec.fp4_encode(v), _fp4_brute(v))
+
+
+def test_mxfp4_block_scales():
+    g = np.random.default_rng(12)
+    w = g.standard_normal((128, 7)) * np.exp2(g.integers(-20, 20, (1, 7)))
+    w[32:64, 3] = 0.0                                    # an all-zero block
+    codes, sb, X = codec.mxfp4_encode(w)
+    assert codes.shape == w.shape and sb.shape == (4, 7)
+    amax = np.abs(w).reshape(4, 32, 7).max(axis=1)
+    nz = amax > 0
+    assert np.all(X == np.ldexp(1.0, sb.astype(int) - 127))          # E8M0: a power of two
+    r = amax[nz] / X[nz]
+    assert np.all((r >= 4.0) & (r < 8.0))                             # largest element exponent 2
+    assert sb[1, 3] == 0 and np.all(codes[32:64, 3] == 0)
+    # every element is the E2M1 rounding of w / X
+    assert np.array_equal(codes, codec.fp4_encode(w / np.repeat(X, 32, axis=0)))
+    dec = codec.mxfp4_decode(codes, sb)
+    Xr = np.repeat(X, 32, axis=0)
+    inside = np.abs(w) <= 6.0 * Xr
+    assert np.all(np.abs(dec - w)[inside] <= Xr[inside])           # half the widest quantum (2 X)
+    assert np.all(dec[~inside] == np.sign(w[~inside]) * 6.0 * Xr[~inside])  # (6X, 8X) saturates
+    # scaling one block by 2**k leaves its codes and moves its scale byte by k
+    w2 = w.copy()
+    w2[64:96, 5] *= 2.0 ** 9
+    c2, sb2, _ = codec.mxfp4_encode(w2)
+    assert np.array_equal(c2, codes) and sb2[2, 5] == sb[2, 5] + 9
+    assert np.array_equal(np.delete(sb2.ravel(), 2 * 7 + 5), np.delete(sb.ravel(), 2 * 7 + 5))
+
+
 def test_e4m3_encode_matches_brute_force_nearest():
     codes, vals = _e4m3_table()
     v = _e4m3_probe_values()
@@ -472,6 +532,20 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     _planted(monkeypatch, codec, "bf16_encode",
              lambda v: orig_b(np_.nextafter(np_.asarray(v, float), 0.0)),
              test_bf16_encode_matches_brute_force_nearest)                  # ties toward zero
+    orig_f4 = codec.fp4_encode
+    _planted(monkeypatch, codec, "fp4_encode",
+             lambda v: orig_f4(np_.nextafter(np_.asarray(v, float), np_.sign(np_.asarray(v, float)) * np_.inf)),
+             test_fp4_encode_matches_brute_force_nearest)                   # ties away from zero
+    def mx_emax3(w):  # block exponent from the wrong element exponent (3 instead of 2)
+        w = np_.asarray(w, float)
+        K, N = w.shape
+        b = w.reshape(K // 32, 32, N)
+        amax = np_.abs(b).max(axis=1)
+        nz = amax > 0
+        e = np_.where(nz, np_.floor(np_.log2(np_.where(nz, amax, 1.0))) - 3, -127).astype(np_.int64)
+        X = np_.ldexp(1.0, e)
+        return codec.fp4_encode(b / X[:, None, :]).reshape(K, N), (e + 127).astype(np_.uint8), X
+    _planted(monkeypatch, codec, "mxfp4_encode", mx_emax3, test_mxfp4_block_scales)
     orig_red = ref.reduce_partials
     _planted(monkeypatch, ref, "reduce_partials",
              lambda p, a=1.0, c=None: orig_red(np_.asarray(p)[:1], a, c),
