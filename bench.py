@@ -66,15 +66,16 @@ def time_gemm(torch, frt, device, synth, M, K, N, dtype, reps=128, pool_bytes=1 
     wbytes = pk.numel()
     ncopy = max(8, int(pool_bytes // wbytes) + 1)
     pool = [pk.clone() for _ in range(ncopy)]
-    a = device.empty_bytes(frt.frt_operand_bytes(dtype, M, K))
+    adt = frt.act_dtype(dtype)  # MXFP4 weights take an e4m3 operand
+    a = device.empty_bytes(frt.frt_operand_bytes(adt, M, K))
     a.zero_()
-    out = device.empty_bytes(frt.frt_operand_bytes(dtype, M, N // 2))
+    out = device.empty_bytes(frt.frt_operand_bytes(adt, M, N // 2))
     splits = 1  # the library's choice for a GEMM that ends in an epilogue
     stream = torch.cuda.current_stream()
 
     def launch(i, st):
         frt.frt_skinny_gemm_splitk(M, N, K, splits, dtype, frt.W_GATE_UP, a, pool[i % ncopy], cs, 1.0,
-                                   None, 0, frt.EPI_SILU_GATE_QUANT, out, dtype, 1.0, stream=st)
+                                   None, 0, frt.EPI_SILU_GATE_QUANT, out, adt, 1.0, stream=st)
     for i in range(ncopy):
         launch(i, stream.cuda_stream)
     torch.cuda.synchronize()
@@ -162,15 +163,17 @@ def state_reuse(torch, chain, synth, dims, packed, wl, reps=20):
                 x_in_refresh_plus_decision_us=round(x_only_us, 1))
 
 
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}  # MI355X dense, published
+# MI355X dense, published.  MXFP4 weights meet e4m3 activations in the FP4 x FP8 form of the
+# block-scaled MFMA, which runs at the FP8 rate, so its peak is FP8's.
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "mxfp4": 5000.0}
 
 
 def gemm_sweep(torch, frt, device, synth):
-    """Gate|up GEMM K=2048, N=16384 over M in {1,10,16,32,50,64}, bf16 and e4m3: the
-    roofline curve (achieved HBM GB/s on weight streaming, MFMA utilisation)."""
+    """Gate|up GEMM K=2048, N=16384 over M in {1,10,16,32,50,64}, bf16, e4m3 and MXFP4
+    weights: the roofline curve (achieved HBM GB/s on weight streaming, MFMA utilisation)."""
     K, N = 2048, 16384
     rows = []
-    for name, dt in (("bf16", frt.BF16), ("e4m3", frt.E4M3)):
+    for name, dt in (("bf16", frt.BF16), ("e4m3", frt.E4M3), ("mxfp4", frt.MXFP4)):
         for M in (1, 10, 16, 32, 50, 64):
             us, nbytes, s = time_gemm(torch, frt, device, synth, M, K, N, dt, reps=64)
             gbs = nbytes / (us * 1e-6) / 1e9
@@ -302,19 +305,23 @@ def main():
         scales = cal.calibrate().cpu().numpy()
         cal.close()
         del packed
-        packed8 = chain.PackedLayers(wl["layers"], dims, frt.E4M3)
-        ch = chain.Chain(dims, packed8, use_graph=True)
-        chain.load_workload(ch, wl, scales)
-        torch.cuda.synchronize()
-        ms = time_chain(torch, ch, args.steps, args.warmup)
-        wb = chain_weight_bytes(dims, 1) + dims["layers"] * 4 * (1280 + 1024 + 8192 + 1024)
-        results[(M, "e4m3", False)] = dict(ms=ms, us_layer=ms * 1e3 / nl, kernels=ch.kernel_count(), dims=dims,
-                                           weight_gbs=(wb + kv_bytes(dims)) * dims["steps"] / (ms * 1e-3) / 1e9,
-                                           finite=bool(np.isfinite(ch.read("x_out")).all()))
-        log(f"M={M} e4m3: {ms:.3f} ms/decision, {ms * 1e3 / nl:.2f} us/layer")
-        ch.close()
-        del packed8, wl
-        torch.cuda.empty_cache()
+        # the same scales serve the MXFP4-weight chain, whose activations are e4m3 too
+        for dt_name, wdt in (("e4m3", frt.E4M3), ("mxfp4", frt.MXFP4)):
+            packed8 = chain.PackedLayers(wl["layers"], dims, wdt)
+            ch = chain.Chain(dims, packed8, use_graph=True)
+            chain.load_workload(ch, wl, scales)
+            torch.cuda.synchronize()
+            ms = time_chain(torch, ch, args.steps, args.warmup)
+            wb = packed8.nbytes() + sum(t.numel() * 4 for v in packed8.s.values() for t in v if t is not None)
+            results[(M, dt_name, False)] = dict(
+                ms=ms, us_layer=ms * 1e3 / nl, kernels=ch.kernel_count(), dims=dims,
+                weight_gbs=(wb + kv_bytes(dims)) * dims["steps"] / (ms * 1e-3) / 1e9,
+                finite=bool(np.isfinite(ch.read("x_out")).all()))
+            log(f"M={M} {dt_name}: {ms:.3f} ms/decision, {ms * 1e3 / nl:.2f} us/layer")
+            ch.close()
+            del packed8
+            torch.cuda.empty_cache()
+        del wl
     best_pf = results[(50, "bf16", True)]["ms"] < results[(50, "bf16", False)]["ms"]
     results[50] = results[(50, "bf16", best_pf)]
     results[10] = results[(10, "bf16", False)]
@@ -357,6 +364,12 @@ def main():
                  "weight_stream_gbs_m50": round(results[(50, "e4m3", False)]["weight_gbs"], 1),
                  "scales": "calibrated on the GPU (one bf16 run on seed-1 inputs)",
                  "outputs_finite": results[(50, "e4m3", False)]["finite"] and results[(10, "e4m3", False)]["finite"]},
+        "mxfp4": {"us_per_layer_m50": round(results[(50, "mxfp4", False)]["us_layer"], 3),
+                  "us_per_layer_m10": round(results[(10, "mxfp4", False)]["us_layer"], 3),
+                  "weight_stream_gbs_m50": round(results[(50, "mxfp4", False)]["weight_gbs"], 1),
+                  "activations": "e4m3, the e4m3 chain's calibrated static scales",
+                  "outputs_finite": results[(50, "mxfp4", False)]["finite"]
+                  and results[(10, "mxfp4", False)]["finite"]},
         "us_per_layer_m10": round(results[10]["us_layer"], 3),
         "ms_per_decision_m10": round(results[10]["ms"], 4),
         "weight_stream_gbs": round(r["weight_gbs"], 1),

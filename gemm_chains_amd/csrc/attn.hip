@@ -161,7 +161,7 @@ __device__ __forceinline__ void attend_block(const KVBlock& b, const bf16x8 (&qf
 // chunk the workgroup writes the quantised output, otherwise an fp32 partial record.
 template <int NW, bool MULTI, bool REC, int ODT>
 __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p) {
-  const int h = blockIdx.x, mb = blockIdx.y, ch = blockIdx.z, nch = gridDim.z;
+  const int h = blockIdx.x, mb = blockIdx.y, ch = blockIdx.z;
   // wave index made provably uniform: MFMAs ignore EXEC, so branches around them must be
   // scalar branches
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -44,7 +44,7 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 static int validate_desc(const frt_chain_desc* d) {
   FRT_CHECK(d, FRT_E_NULL);
   FRT_CHECK(d->layers >= 1 && d->layers <= 256 && d->steps >= 1 && d->steps <= 1000, FRT_E_SHAPE);
-  FRT_CHECK(is_ab_dtype(d->dtype), FRT_E_DTYPE);
+  FRT_CHECK(is_w_dtype(d->dtype), FRT_E_DTYPE);
   const int ks = kstep_of(d->dtype);
   FRT_CHECK(d->M >= 1 && d->M <= kMaxM, FRT_E_SHAPE);
   FRT_CHECK(d->hidden >= ks && d->hidden % ks == 0 && d->hidden <= kMaxProducerK, FRT_E_SHAPE);
@@ -88,10 +88,11 @@ static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
   FRT_CHECK((H / ks) % L.s_qkv == 0 && (L.nattn / ks) % L.s_o == 0 && (H / ks) % L.s_up == 0 &&
                 (F / ks) % L.s_down == 0,
             FRT_E_SPLITK);
-  L.op_qkv = frt_operand_bytes(dt, M, H);
-  L.op_o = frt_operand_bytes(dt, M, L.nattn);
-  L.op_up = frt_operand_bytes(dt, M, H);
-  L.op_down = frt_operand_bytes(dt, M, F);
+  const int adt = act_dtype_of(dt);  // GEMM operand format
+  L.op_qkv = frt_operand_bytes(adt, M, H);
+  L.op_o = frt_operand_bytes(adt, M, L.nattn);
+  L.op_up = frt_operand_bytes(adt, M, H);
+  L.op_down = frt_operand_bytes(adt, M, F);
   L.kv_len = d->prefix_len + M;
   L.ldv = (L.kv_len + 31) / 32 * 32;
   L.pq = L.s_qkv > 1 ? (size_t)L.s_qkv * M * L.nqkv * 4 : 0;
@@ -172,13 +173,15 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
   const frt_chain_desc& d = c->d;
   const ChainLayout& L = c->L;
   const int M = d.M, H = d.hidden, F = d.mlp, MB = m_blocks(M);
-  const bool e4 = d.dtype == FRT_E4M3;
+  const bool e4 = d.dtype == FRT_E4M3;          // weights carry column scales
+  const int adt = act_dtype_of(d.dtype);        // GEMM operand format
+  const bool aq = adt == FRT_E4M3;              // operands carry static activation scales
   const bool dbg = d.keep_intermediates != 0;
   const size_t modsz = (size_t)3 * H;  // floats per (step, layer, sublayer)
   float* mod = (float*)at(c, L.mod);
   float* act = (float*)at(c, L.act);
   auto modp = [&](int k, int l, int sub, int row) { return mod + (((size_t)k * d.layers + l) * 2 + sub) * modsz + (size_t)row * H; };
-  auto actp = [&](int l, int site) -> const float* { return e4 ? act + l * 4 + site : nullptr; };
+  auto actp = [&](int l, int site) -> const float* { return aq ? act + l * 4 + site : nullptr; };
   int n = 0;
   const bool pf = d.prefetch_next != 0;
   unsigned* sink = (unsigned*)at(c, L.sink);
@@ -222,7 +225,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
       gu.N = 2 * F; gu.K = H; gu.splits = L.s_up; gu.ksteps_per_split = H / kstep_of(d.dtype) / L.s_up;
       gu.layout = FRT_W_GATE_UP; gu.a = a_up; gu.w = (const uint8_t*)c->wu[l]; gu.colscale = e4 ? c->su[l] : nullptr;
       gu.act_scale_ptr = actp(l, SITE_UP);
-      gu.out_dtype = d.dtype; gu.out_scale = 1.f; gu.out_scale_ptr = actp(l, SITE_DOWN);
+      gu.out_dtype = adt; gu.out_scale = 1.f; gu.out_scale_ptr = actp(l, SITE_DOWN);
       gu.amax = amax ? amax + l * 4 + SITE_DOWN : nullptr;
       if (L.s_up == 1) {
         gu.epi = FRT_EPI_SILU_GATE_QUANT; gu.out = a_down; gu.partials = nullptr;
@@ -245,7 +248,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
       a.residual = h_prev; a.residual_out = h_attn;
       a.gate = pdown_prev ? modp(kp, lp, 1, MOD_GATE) : nullptr;
       a.ada_scale = modp(k, l, 0, MOD_SCALE); a.ada_shift = modp(k, l, 0, MOD_SHIFT);
-      a.eps = d.eps; a.out_dtype = d.dtype; a.act_scale = 1.f; a.act_scale_ptr = actp(l, SITE_QKV);
+      a.eps = d.eps; a.out_dtype = adt; a.act_scale = 1.f; a.act_scale_ptr = actp(l, SITE_QKV);
       a.operand = a_qkv;
       a.amax = amax ? amax + l * 4 + SITE_QKV : nullptr;
       a.sink = sink;
@@ -265,7 +268,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
       AttnParams t{};
       t.M = M; t.MB = MB; t.n_heads = d.n_heads; t.kv_len = L.kv_len;
       t.q = qbuf; t.k = kcl; t.vt = vcl; t.ldv = L.ldv;
-      t.out_dtype = d.dtype; t.out_scale = 1.f; t.out_scale_ptr = actp(l, SITE_O);
+      t.out_dtype = adt; t.out_scale = 1.f; t.out_scale_ptr = actp(l, SITE_O);
       t.operand = a_o; t.workspace = (float*)at(c, L.aws);
       t.amax = amax ? amax + l * 4 + SITE_O : nullptr;
       FRT_HIP(launch_attention(t, s)); n += attention_kernel_count(L.kv_len);
@@ -293,7 +296,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
         ReduceParams r{};
         r.M = M; r.N = 2 * F; r.MB = MB; r.splits = L.s_up; r.partials = gu.partials;
         r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_UP); r.colscale = gu.colscale;
-        r.epi = FRT_EPI_SILU_GATE_QUANT; r.out = a_down; r.out_dtype = d.dtype; r.out_scale = 1.f;
+        r.epi = FRT_EPI_SILU_GATE_QUANT; r.out = a_down; r.out_dtype = adt; r.out_scale = 1.f;
         r.out_scale_ptr = actp(l, SITE_DOWN); r.amax = gu.amax;
         FRT_HIP(launch_reduce(r, s)); ++n;
       }
@@ -312,7 +315,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
   f.M = M; f.K = H; f.MB = MB; f.x = pdown_prev; f.x_splits = L.s_down; f.x_scale = 1.f;
   f.x_scale_ptr = actp(lp, SITE_DOWN); f.x_colscale = e4 ? c->sd[lp] : nullptr;
   f.residual = h_prev; f.residual_out = (float*)at(c, L.x_out); f.gate = modp(kp, lp, 1, MOD_GATE);
-  f.eps = d.eps; f.out_dtype = d.dtype; f.act_scale = 1.f; f.operand = nullptr;
+  f.eps = d.eps; f.out_dtype = adt; f.act_scale = 1.f; f.operand = nullptr;
   FRT_HIP(launch_rnq(f, s)); ++n;
   if (count) *count = n;
   return FRT_OK;

@@ -37,11 +37,17 @@ void set_hip_error(int e);
 inline bool aligned16(const void* p) { return (((uintptr_t)p) & 15u) == 0; }
 inline int elem_bytes(int dtype) { return dtype == FRT_BF16 ? 2 : (dtype == FRT_E4M3 ? 1 : 4); }
 inline bool is_ab_dtype(int dtype) { return dtype == FRT_BF16 || dtype == FRT_E4M3; }
+// Weight formats of a GEMM, and the operand (activation) format each one multiplies.
+inline bool is_w_dtype(int dtype) { return is_ab_dtype(dtype) || dtype == FRT_MXFP4; }
+__host__ __device__ constexpr int act_dtype_of(int wdtype) { return wdtype == FRT_MXFP4 ? FRT_E4M3 : wdtype; }
 inline bool is_split(int s) { return s == 1 || s == 2 || s == 4 || s == 8 || s == 16; }
 inline int m_blocks(int M) { return (M + 15) / 16; }
-// Elements of K covered by one MFMA k-step (and one packed tile): 32 bf16, 128 e4m3.
-__host__ __device__ inline int kstep_of(int dtype) { return dtype == FRT_BF16 ? 32 : 128; }
-__host__ __device__ inline int tile_bytes_of(int dtype) { return dtype == FRT_BF16 ? 1024 : 2048; }
+// Elements of K covered by one MFMA k-step (and one packed tile): 32 bf16, 128 e4m3/MXFP4.
+__host__ __device__ constexpr int kstep_of(int dtype) { return dtype == FRT_BF16 ? 32 : 128; }
+// Bytes of one packed tile (16 rows or columns x one k-step).
+__host__ __device__ constexpr int tile_bytes_of(int dtype) {
+  return dtype == FRT_BF16 ? 1024 : (dtype == FRT_MXFP4 ? 1088 : 2048);
+}
 inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
   uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -51,10 +57,15 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // ------------------------------------------------------------------ packed layouts
 // Packed GEMM operand (activations), Mp = 16*MB rows, logical A[m][k]:
 //   one tile per (m-block mb, k-step ks) at byte (ks*MB + mb)*TB, so the MB tiles a GEMM
-//   wave needs for one k-step are adjacent.  Inside a tile, MFMA lane L (0..63) owns the
-//   16 bytes at L*16 (bf16) or the two 16-byte halves at h*1024 + L*16 (e4m3), holding
-//   row m = 16*mb + L%16 and k = ks*KS + (L/16)*(KS/4) + [0, KS/4) in increasing order
-//   (KS = 32 or 128); the e4m3 lane's 32 bytes are split into two halves of 16 k each.
+//   wave needs for one k-step are adjacent.  Inside a tile, MFMA lane L (0..63) owns row
+//   m = 16*mb + L%16 and, with g = L/16:
+//   - bf16 (k-step 32): the 16 bytes at L*16, k = ks*32 + 8g + [0, 8);
+//   - e4m3 (k-step 128): two 16-byte halves h at h*1024 + L*16, half h holding
+//     k = ks*128 + 64h + 16g + [0, 16).  (This order makes the 32 FP4 elements an MXFP4
+//     weight lane pairs with, measured on gfx950's FP4 x FP8 block-scaled MFMA, the
+//     contiguous k range 32g' + [0, 32) of weight lane group g' -- one OCP MX block, under
+//     that lane's scale.  FP8 x FP8 pairs byte p of A lane L with byte p of B lane L, so
+//     any order shared by both operands gives the same contraction.)
 __host__ __device__ inline size_t operand_offset(int dtype, int MB, int m, int k) {
   const int mb = m >> 4, r = m & 15;
   if (dtype == FRT_BF16) {
@@ -63,8 +74,8 @@ __host__ __device__ inline size_t operand_offset(int dtype, int MB, int m, int k
     return ((size_t)ks * MB + mb) * 1024 + (size_t)lane * 16 + (size_t)(kk & 7) * 2;
   }
   const int ks = k >> 7, kk = k & 127;
-  const int lane = r + 16 * (kk >> 5);
-  const int half = (kk >> 4) & 1;
+  const int lane = r + 16 * ((kk >> 4) & 3);
+  const int half = kk >> 6;
   return ((size_t)ks * MB + mb) * 2048 + (size_t)half * 1024 + (size_t)lane * 16 + (kk & 15);
 }
 
@@ -92,9 +103,26 @@ __host__ __device__ inline size_t weight_offset(int dtype, int layout, int K, in
     return ((size_t)pt * (K >> 5) + ks) * 1024 + (size_t)lane * 16 + (size_t)(kk & 7) * 2;
   }
   const int ks = k >> 7, kk = k & 127;
-  const int lane = r + 16 * (kk >> 5);
-  const int half = (kk >> 4) & 1;
+  const int lane = r + 16 * ((kk >> 4) & 3);
+  const int half = kk >> 6;
   return ((size_t)pt * (K >> 7) + ks) * 2048 + (size_t)half * 1024 + (size_t)lane * 16 + (kk & 15);
+}
+
+// Packed MXFP4 weight: 1088-byte tiles in the same (pt, ks) order.  Lane L of a tile
+// holds column n = 16*lt + L%16 and the OCP MX block g = L/16 of the k-step, k = ks*128 +
+// 32g + q for q = 0..31: FP4 code q in byte L*16 + q/2 (even q in the low nibble), its
+// E8M0 scale byte at 1024 + L.  This is the operand order the FP4 x FP8 MFMA pairs with
+// the e4m3 activation order above, and one lane's scale covers exactly its own block.
+__host__ __device__ inline size_t mx_tile_offset(int layout, int K, int N, int k, int n) {
+  return ((size_t)packed_tile_of(layout, N, n >> 4) * (K >> 7) + (k >> 7)) * 1088;
+}
+__host__ __device__ inline size_t mx_code_byte(int layout, int K, int N, int k, int n) {
+  const int lane = (n & 15) + 16 * ((k >> 5) & 3);
+  return mx_tile_offset(layout, K, N, k, n) + (size_t)lane * 16 + ((k & 31) >> 1);
+}
+__host__ __device__ inline size_t mx_scale_byte(int layout, int K, int N, int k, int n) {
+  const int lane = (n & 15) + 16 * ((k >> 5) & 3);
+  return mx_tile_offset(layout, K, N, k, n) + 1024 + lane;
 }
 
 // ------------------------------------------------------------------ number formats (device)

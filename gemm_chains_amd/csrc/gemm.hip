@@ -76,12 +76,13 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const ReduceParams p
 }
 
 // ------------------------------------------------------------------ launch plumbing
-// Frag registers per lane: 4 (bf16) or 8 (e4m3) per tile per k-step.  A round's loads
-// stay within ~192 VGPRs so that every one of them can be in flight at once.
+// Frag registers per lane and k-step: 4 (bf16), 8 (e4m3), 5 (MXFP4 codes + scale) per
+// weight tile, 4 or 8 per operand tile.  A round's loads stay within ~192 VGPRs so that
+// every one of them can be in flight at once.
 static int per_max(int dtype, int nt, int mbw) {
-  const int v = dtype == FRT_BF16 ? 4 : 8;
+  const int v = nt * frag_regs(dtype) + mbw * frag_regs(act_dtype_of(dtype));
   int per = 8;
-  while (per > 1 && per * (nt + mbw) * v > 192) per /= 2;
+  while (per > 1 && per * v > 192) per /= 2;
   return per;
 }
 
@@ -125,7 +126,7 @@ WeightTouch gemm_weight_touch(const GemmParams& p, int part, int parts) {
   const GemmShape sh = choose_shape(p);
   WeightTouch t{};
   t.w = p.w;
-  t.tb = p.ab_dtype == FRT_BF16 ? 1024 : 2048;
+  t.tb = tile_bytes_of(p.ab_dtype);
   t.ks = p.K / kstep_of(p.ab_dtype);
   t.nt = sh.nt;
   t.kps = p.ksteps_per_split;
@@ -145,7 +146,11 @@ hipError_t launch_gemm(const GemmParams& p_in, hipStream_t s) {
   p.ksteps = p.K / kstep_of(p.ab_dtype);
   p.row_groups = sh.row_groups;
   p.col_groups = sh.col_groups;
-  return p.ab_dtype == FRT_BF16 ? launch_gemm_typed<FRT_BF16>(p, sh, s) : launch_gemm_typed<FRT_E4M3>(p, sh, s);
+  switch (p.ab_dtype) {
+    case FRT_BF16: return launch_gemm_typed<FRT_BF16>(p, sh, s);
+    case FRT_E4M3: return launch_gemm_typed<FRT_E4M3>(p, sh, s);
+    default: return launch_gemm_typed<FRT_MXFP4>(p, sh, s);
+  }
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
@@ -203,7 +208,7 @@ static size_t epilogue_out_bytes(int M, int N, int epi, int out_dtype) {
 }
 
 extern "C" int frt_splitk_choose(int M, int N, int K, int ab_dtype) {
-  if (M < 1 || M > kMaxM || N < 16 || N % 16 || !is_ab_dtype(ab_dtype) || K < kstep_of(ab_dtype) ||
+  if (M < 1 || M > kMaxM || N < 16 || N % 16 || !is_w_dtype(ab_dtype) || K < kstep_of(ab_dtype) ||
       K % kstep_of(ab_dtype))
     return 0;
   return choose_splits(M, N, K, ab_dtype, FRT_EPI_NONE);
@@ -215,7 +220,7 @@ extern "C" int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int spl
                                       size_t partials_bytes, int epi, void* out_dev, int out_dtype,
                                       float out_act_scale) {
   FRT_CHECK(a_packed_dev && w_packed_dev, FRT_E_NULL);
-  FRT_CHECK(is_ab_dtype(ab_dtype), FRT_E_DTYPE);
+  FRT_CHECK(is_w_dtype(ab_dtype), FRT_E_DTYPE);
   FRT_CHECK(M >= 1 && M <= kMaxM, FRT_E_SHAPE);
   FRT_CHECK(N >= 16 && N % 16 == 0 && N <= (1 << 20), FRT_E_SHAPE);
   FRT_CHECK(K >= kstep_of(ab_dtype) && K % kstep_of(ab_dtype) == 0 && K <= (1 << 16), FRT_E_SHAPE);
@@ -239,7 +244,7 @@ extern "C" int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int spl
     FRT_CHECK(partials_dev, FRT_E_NULL);
     FRT_CHECK(partials_bytes >= pbytes, FRT_E_WORKSPACE);
   }
-  const size_t ab = frt_operand_bytes(ab_dtype, M, K);
+  const size_t ab = frt_operand_bytes(act_dtype_of(ab_dtype), M, K);
   const size_t wb = frt_weight_bytes(ab_dtype, K, N);
   const size_t ob = epilogue_out_bytes(M, N, epi, out_dtype);
   if (need_partials) {
@@ -298,7 +303,7 @@ extern "C" int frt_skinny_gemm_qkv(void* stream, int M, int K, int n_heads, int 
                                    uint16_t* k_out_dev, uint16_t* v_t_out_dev, int v_ld) {
   uint16_t* v_out_dev = v_t_out_dev;
   FRT_CHECK(a_packed_dev && w_packed_dev && q_out_dev && k_out_dev && v_out_dev, FRT_E_NULL);
-  FRT_CHECK(is_ab_dtype(ab_dtype), FRT_E_DTYPE);
+  FRT_CHECK(is_w_dtype(ab_dtype), FRT_E_DTYPE);
   FRT_CHECK(M >= 1 && M <= kMaxM, FRT_E_SHAPE);
   FRT_CHECK(n_heads >= 1 && n_heads <= 64 && head_dim >= 16 && head_dim % 16 == 0, FRT_E_SHAPE);
   FRT_CHECK(v_ld >= M, FRT_E_SHAPE);
@@ -317,7 +322,7 @@ extern "C" int frt_skinny_gemm_qkv(void* stream, int M, int K, int n_heads, int 
     FRT_CHECK(partials_dev, FRT_E_NULL);
     FRT_CHECK(partials_bytes >= pbytes, FRT_E_WORKSPACE);
   }
-  const size_t ab = frt_operand_bytes(ab_dtype, M, K), wb = frt_weight_bytes(ab_dtype, K, N);
+  const size_t ab = frt_operand_bytes(act_dtype_of(ab_dtype), M, K), wb = frt_weight_bytes(ab_dtype, K, N);
   const size_t qb = (size_t)M * n_heads * head_dim * 2, kb = (size_t)M * head_dim * 2;
   const size_t vb = ((size_t)(head_dim - 1) * v_ld + M) * 2;
   const void* outs[] = {q_out_dev, k_out_dev, v_out_dev};

@@ -1,5 +1,5 @@
-// Skinny split-K GEMM kernel template (instantiated per operand type in gemm_bf16.hip
-// and gemm_e4m3.hip; host side in gemm.hip).
+// Skinny split-K GEMM kernel template (instantiated per weight format in gemm_bf16.hip,
+// gemm_e4m3.hip and gemm_mxfp4.hip; host side in gemm.hip).
 //
 // Pages: observation-age notes ("思考探索：具身推理加速，先看动作执行时观测有多旧"),
 // section "小 M GEMM 要看并行度，也要看归约代价" (C = A W with few rows, cut along K into
@@ -39,8 +39,17 @@ template <>
 struct Frag<FRT_E4M3> {
   u32x4 v0, v1;
 };
+template <>
+struct Frag<FRT_MXFP4> {
+  u32x4 v;     // 32 FP4 codes: one OCP MX block
+  unsigned s;  // its E8M0 scale byte
+};
 
-// One MFMA operand tile per wave: 16 bytes per lane (bf16) or two 16-byte halves (e4m3).
+// VGPRs a fragment holds per lane (the register budget of a round's loads).
+constexpr int frag_regs(int dt) { return dt == FRT_BF16 ? 4 : (dt == FRT_MXFP4 ? 5 : 8); }
+
+// One MFMA operand tile per wave: 16 bytes per lane (bf16), two 16-byte halves (e4m3),
+// or 16 bytes of FP4 codes plus the lane's scale byte (MXFP4).
 // STREAM marks weight loads non-temporal so the single-use weight stream does not evict
 // the activation tiles every workgroup re-reads from L2.  (A compile-time choice: two
 // loads of one address behind a run-time select get merged and lose the hint.)
@@ -50,6 +59,10 @@ __device__ __forceinline__ void load_frag(Frag<DT>& f, const uint8_t* tile, int 
   if constexpr (DT == FRT_BF16) {
     if constexpr (STREAM) f.v = __builtin_nontemporal_load(p0);
     else f.v = *p0;
+  } else if constexpr (DT == FRT_MXFP4) {
+    static_assert(STREAM, "MXFP4 is a weight format");
+    f.v = __builtin_nontemporal_load(p0);
+    f.s = __builtin_nontemporal_load(tile + 1024 + lane);
   } else {
     const u32x4* p1 = reinterpret_cast<const u32x4*>(tile + 1024 + lane * 16);
     if constexpr (STREAM) {
@@ -75,6 +88,16 @@ __device__ __forceinline__ f32x4 mma(const Frag<FRT_E4M3>& w, const Frag<FRT_E4M
   // format 0/0 = OCP e4m3 for both operands; E8M0 block scales 127 = 2^0 (unscaled)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, aa, c, 0, 0, 0, 127, 0, 127);
 }
+__device__ __forceinline__ f32x4 mma(const Frag<FRT_MXFP4>& w, const Frag<FRT_E4M3>& a, f32x4 c) {
+  i32x8 wa, aa;
+  wa[0] = (int)w.v.x; wa[1] = (int)w.v.y; wa[2] = (int)w.v.z; wa[3] = (int)w.v.w;
+  wa[4] = 0; wa[5] = 0; wa[6] = 0; wa[7] = 0;  // an FP4 operand is four dwords
+  aa[0] = (int)a.v0.x; aa[1] = (int)a.v0.y; aa[2] = (int)a.v0.z; aa[3] = (int)a.v0.w;
+  aa[4] = (int)a.v1.x; aa[5] = (int)a.v1.y; aa[6] = (int)a.v1.z; aa[7] = (int)a.v1.w;
+  // format 4 = FP4 E2M1 weights under the lane's own E8M0 block scale, format 0 = e4m3
+  // activations unscaled (their static scale is applied after the sum)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, aa, c, 4, 0, 0, (int)w.s, 0, 127);
+}
 
 // SiLU(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (a few ulp; the parity
 // tie band is 2^-17 of the summands).
@@ -93,7 +116,9 @@ __device__ __forceinline__ float silu_f(float g) {
 // to all of them after one HBM read) spread GEMMs with few column tiles over more CUs.
 template <int DT, int MB, int NT, int PER, int EPI>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
-  constexpr int TB = DT == FRT_BF16 ? 1024 : 2048;
+  constexpr int ADT = act_dtype_of(DT);   // operand (activation) format
+  constexpr int TBW = tile_bytes_of(DT);  // weight tile bytes
+  constexpr int TB = tile_bytes_of(ADT);  // operand tile bytes
   constexpr int NF = NT * MB;
   extern __shared__ f32x4 red[];  // [kwaves][NF][64]
 
@@ -120,7 +145,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
 
   const uint8_t* wbase[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) wbase[t] = p.w + (size_t)(g * NT + t) * KS * TB;
+  for (int t = 0; t < NT; ++t) wbase[t] = p.w + (size_t)(g * NT + t) * KS * TBW;
   const uint8_t* abase = p.a + (size_t)mb0 * TB;
   const size_t astep = (size_t)p.MB * TB;
 
@@ -133,13 +158,13 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
   int ks0 = ks_begin;
   do {  // run = PER * rounds, rounds >= 1
     Frag<DT> wf[PER][NT];
-    Frag<DT> af[PER][MB];
+    Frag<ADT> af[PER][MB];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) load_frag<DT, true>(wf[u][t], wbase[t] + (size_t)(ks0 + u) * TB, lane);
+      for (int t = 0; t < NT; ++t) load_frag<DT, true>(wf[u][t], wbase[t] + (size_t)(ks0 + u) * TBW, lane);
 #pragma unroll
-      for (int b = 0; b < MB; ++b) load_frag<DT, false>(af[u][b], abase + (size_t)(ks0 + u) * astep + (size_t)b * TB, lane);
+      for (int b = 0; b < MB; ++b) load_frag<ADT, false>(af[u][b], abase + (size_t)(ks0 + u) * astep + (size_t)b * TB, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -225,7 +250,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
 template <int DT, int MB, int NT, int PER, int EPI>
 static hipError_t launch_t(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
   constexpr bool silu = EPI == kGemmSiluBf16 || EPI == kGemmSiluE4m3;
-  if constexpr (PER * (NT + MB) * (DT == FRT_BF16 ? 4 : 8) > 192 || (silu && NT % 2)) {
+  if constexpr (PER * (NT * frag_regs(DT) + MB * frag_regs(act_dtype_of(DT))) > 192 || (silu && NT % 2)) {
     return hipErrorInvalidValue;  // never chosen (register budget / SiLU pairs): not instantiated
   } else {
     const dim3 grid = sh.row_groups == 1 ? dim3(sh.col_groups, 1, p.splits)

@@ -49,7 +49,8 @@ __global__ void __launch_bounds__(256) pack_weight_kernel(const uint16_t* __rest
   }
   const int pt = (int)(tile / KS), ks = (int)(tile % KS);
   const int n = logical_tile_of(layout, N, pt) * 16 + (lane & 15);
-  const int k0 = ks * KSTEP + (lane >> 4) * (KSTEP / 4) + half * 16;
+  // first k of the slot (the operand_offset / weight_offset order)
+  const int k0 = dtype == FRT_BF16 ? ks * 32 + 8 * (lane >> 4) : ks * 128 + 64 * half + 16 * (lane >> 4);
   u32x4 v;
   uint32_t* vw = reinterpret_cast<uint32_t*>(&v);
   // W' = gamma * W and W' / s_w are formed in float64 (the product is exact, the quotient
@@ -82,6 +83,63 @@ __global__ void __launch_bounds__(256) pack_weight_kernel(const uint16_t* __rest
   *reinterpret_cast<u32x4*>(out + slot * 16) = v;
 }
 
+// FP4 E2M1 code of a float64 value: round to the nearest of the eight magnitudes
+// {0, 0.5, 1, 1.5, 2, 3, 4, 6} (code order), a tie going to the even code (mantissa bit
+// 0), and anything at or past 6 saturating to code 7; the sign is bit 3 (-0 keeps it).
+// Counting the midpoints a magnitude passes gives the code directly.
+__device__ inline uint32_t fp4_code_exact(double x) {
+  const double a = fabs(x);
+  const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) c += (a > mid[i] || (a == mid[i] && ((i + 1) & 1) == 0)) ? 1u : 0u;
+  return c | (signbit(x) ? 8u : 0u);
+}
+
+// MXFP4 weight packing: one thread per lane slot, i.e. one OCP MX block (32 consecutive
+// k of one column).  W' = gamma * W is exact in float64; the block's E8M0 exponent is
+// floor(log2 max|W'|) - 2 (clamped to [-127, 127]; 0 for an all-zero block) and
+// W' / 2^e is exact in float64, so every code is rounded once.
+__global__ void __launch_bounds__(256) pack_mxfp4_kernel(const uint16_t* __restrict__ w, const float* __restrict__ gamma,
+                                                         int K, int N, int layout, uint8_t* __restrict__ out) {
+  const size_t slot = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nslots = (size_t)(K / 32) * N;
+  if (slot >= nslots) return;
+  const int KS = K / 128;
+  const size_t tile = slot / 64;
+  const int lane = (int)(slot % 64);
+  const int pt = (int)(tile / KS), ks = (int)(tile % KS);
+  const int n = logical_tile_of(layout, N, pt) * 16 + (lane & 15);
+  const int k0 = ks * 128 + 32 * (lane >> 4);
+  double v[32];
+  double amax = 0.0;
+#pragma unroll
+  for (int q = 0; q < 32; ++q) {
+    v[q] = (double)bf16_to_f32(w[(size_t)(k0 + q) * N + n]);
+    if (gamma) v[q] *= (double)gamma[k0 + q];
+    amax = fmax(amax, fabs(v[q]));
+  }
+  int e = -127;
+  if (amax > 0.0) {
+    int ex;
+    frexp(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+    e = ex - 1 - 2;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  }
+  u32x4 codes;
+  uint32_t* cw = reinterpret_cast<uint32_t*>(&codes);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= fp4_code_exact(ldexp(v[8 * d + j], -e)) << (4 * j);
+    cw[d] = word;
+  }
+  uint8_t* t = out + tile * 1088;
+  *reinterpret_cast<u32x4*>(t + lane * 16) = codes;
+  t[1024 + lane] = (uint8_t)(e + 127);
+}
+
 }  // namespace frt
 
 using namespace frt;
@@ -92,7 +150,8 @@ extern "C" size_t frt_operand_bytes(int dtype, int M, int K) {
 }
 
 extern "C" size_t frt_weight_bytes(int dtype, int K, int N) {
-  if (!is_ab_dtype(dtype) || K < 1 || N < 1) return 0;
+  if (!is_w_dtype(dtype) || K < 1 || N < 1) return 0;
+  if (dtype == FRT_MXFP4) return K % 128 ? 0 : (size_t)K * N / 2 + (size_t)(K / 32) * N;
   return (size_t)K * N * elem_bytes(dtype);
 }
 
@@ -104,7 +163,7 @@ static int check_operand_shape(int dtype, int M, int K) {
 }
 
 static int check_weight_shape(int dtype, int K, int N, int layout) {
-  FRT_CHECK(is_ab_dtype(dtype), FRT_E_DTYPE);
+  FRT_CHECK(is_w_dtype(dtype), FRT_E_DTYPE);
   FRT_CHECK(K >= kstep_of(dtype) && K % kstep_of(dtype) == 0, FRT_E_SHAPE);
   FRT_CHECK(N >= 16 && N % 16 == 0, FRT_E_SHAPE);
   FRT_CHECK(layout == FRT_W_PLAIN || layout == FRT_W_GATE_UP, FRT_E_ARG);
@@ -138,6 +197,7 @@ extern "C" int frt_operand_unpack_host(const void* packed_host, int dtype, int M
 
 extern "C" int frt_weight_pack_host(const void* codes_host, int dtype, int K, int N, int layout, void* packed_host) {
   FRT_CHECK(codes_host && packed_host, FRT_E_NULL);
+  FRT_CHECK(is_ab_dtype(dtype), FRT_E_DTYPE);  // MXFP4: frt_weight_pack_mxfp4_host
   int st = check_weight_shape(dtype, K, N, layout);
   if (st) return st;
   const int esz = elem_bytes(dtype);
@@ -150,6 +210,7 @@ extern "C" int frt_weight_pack_host(const void* codes_host, int dtype, int K, in
 
 extern "C" int frt_weight_unpack_host(const void* packed_host, int dtype, int K, int N, int layout, void* codes_host) {
   FRT_CHECK(codes_host && packed_host, FRT_E_NULL);
+  FRT_CHECK(is_ab_dtype(dtype), FRT_E_DTYPE);
   int st = check_weight_shape(dtype, K, N, layout);
   if (st) return st;
   const int esz = elem_bytes(dtype);
@@ -157,6 +218,36 @@ extern "C" int frt_weight_unpack_host(const void* packed_host, int dtype, int K,
     for (int n = 0; n < N; ++n)
       memcpy((uint8_t*)codes_host + ((size_t)k * N + n) * esz,
              (const uint8_t*)packed_host + weight_offset(dtype, layout, K, N, k, n), esz);
+  return FRT_OK;
+}
+
+extern "C" int frt_weight_pack_mxfp4_host(const uint8_t* codes_host, const uint8_t* scales_host, int K, int N,
+                                          int layout, void* packed_host) {
+  FRT_CHECK(codes_host && scales_host && packed_host, FRT_E_NULL);
+  int st = check_weight_shape(FRT_MXFP4, K, N, layout);
+  if (st) return st;
+  uint8_t* out = (uint8_t*)packed_host;
+  memset(out, 0, frt_weight_bytes(FRT_MXFP4, K, N));
+  for (int k = 0; k < K; ++k)
+    for (int n = 0; n < N; ++n) {
+      const uint32_t c = codes_host[(size_t)k * N + n] & 15u;
+      out[mx_code_byte(layout, K, N, k, n)] |= (uint8_t)(c << (4 * (k & 1)));
+      if (k % 32 == 0) out[mx_scale_byte(layout, K, N, k, n)] = scales_host[(size_t)(k / 32) * N + n];
+    }
+  return FRT_OK;
+}
+
+extern "C" int frt_weight_unpack_mxfp4_host(const void* packed_host, int K, int N, int layout, uint8_t* codes_host,
+                                            uint8_t* scales_host) {
+  FRT_CHECK(codes_host && scales_host && packed_host, FRT_E_NULL);
+  int st = check_weight_shape(FRT_MXFP4, K, N, layout);
+  if (st) return st;
+  const uint8_t* in = (const uint8_t*)packed_host;
+  for (int k = 0; k < K; ++k)
+    for (int n = 0; n < N; ++n) {
+      codes_host[(size_t)k * N + n] = (uint8_t)((in[mx_code_byte(layout, K, N, k, n)] >> (4 * (k & 1))) & 15u);
+      if (k % 32 == 0) scales_host[(size_t)(k / 32) * N + n] = in[mx_scale_byte(layout, K, N, k, n)];
+    }
   return FRT_OK;
 }
 
@@ -175,6 +266,13 @@ extern "C" int frt_pack_weight(void* stream, int K, int N, const uint16_t* w_bf1
     FRT_CHECK(!overlaps(colscale_dev, (size_t)N * 4, w_bf16_dev, wb), FRT_E_ALIAS);
   }
   hipStream_t s = (hipStream_t)stream;
+  if (dtype == FRT_MXFP4) {
+    const size_t nslots = (size_t)(K / 32) * N;
+    hipLaunchKernelGGL(pack_mxfp4_kernel, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s, w_bf16_dev,
+                       gamma_dev, K, N, layout, (uint8_t*)w_packed_dev);
+    FRT_HIP(hipGetLastError());
+    return FRT_OK;
+  }
   if (dtype == FRT_E4M3) {
     hipLaunchKernelGGL(colscale_kernel, dim3((N + 255) / 256), dim3(256), 0, s, w_bf16_dev, gamma_dev, K, N, colscale_dev);
     FRT_HIP(hipGetLastError());

@@ -11,10 +11,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfrt.so")
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_SPLITK, E_WORKSPACE, E_ALIAS, E_STATE, E_HIP, E_ARG = range(11)
-BF16, E4M3, F32 = 1, 2, 3
+BF16, E4M3, F32, MXFP4 = 1, 2, 3, 4
 W_PLAIN, W_GATE_UP = 0, 1
 EPI_NONE, EPI_STORE_F32, EPI_STORE_BF16, EPI_SILU_GATE_QUANT = 0, 1, 2, 3
-DTYPES = {"bf16": BF16, "e4m3": E4M3, "f32": F32}
+DTYPES = {"bf16": BF16, "e4m3": E4M3, "f32": F32, "mxfp4": MXFP4}
+
+
+def act_dtype(wdtype):
+    """GEMM operand format that goes with a weight format (MXFP4 weights take e4m3)."""
+    return E4M3 if wdtype == MXFP4 else wdtype
 
 _c_void_p = ctypes.c_void_p
 _int = ctypes.c_int
@@ -52,6 +57,8 @@ _SIGS = {
     "frt_operand_unpack_host": (_int, [_c_void_p, _int, _int, _int, _c_void_p]),
     "frt_weight_pack_host": (_int, [_c_void_p, _int, _int, _int, _int, _c_void_p]),
     "frt_weight_unpack_host": (_int, [_c_void_p, _int, _int, _int, _int, _c_void_p]),
+    "frt_weight_pack_mxfp4_host": (_int, [_c_void_p, _c_void_p, _int, _int, _int, _c_void_p]),
+    "frt_weight_unpack_mxfp4_host": (_int, [_c_void_p, _int, _int, _int, _c_void_p, _c_void_p]),
     "frt_pack_weight": (_int, [_c_void_p, _int, _int, _c_void_p, _c_void_p, _int, _int, _c_void_p, _c_void_p]),
     "frt_residual_norm_quant": (_int, [_c_void_p, _int, _int, _c_void_p, _int, _float, _c_void_p, _c_void_p,
                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _float, _int, _float,
@@ -174,6 +181,28 @@ def frt_weight_unpack_host(packed, dtype, K, N, layout=W_PLAIN):
     _check(_lib().frt_weight_unpack_host(_np_ptr(packed), dtype, K, N, layout, _np_ptr(out)),
            "frt_weight_unpack_host")
     return out
+
+
+def frt_weight_pack_mxfp4_host(codes, scales, K, N, layout=W_PLAIN):
+    """codes [K][N] FP4 codes (uint8, low 4 bits), scales [K/32][N] E8M0 bytes -> packed bytes."""
+    import numpy as np
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    out = np.zeros(frt_weight_bytes(MXFP4, K, N), np.uint8)
+    _check(_lib().frt_weight_pack_mxfp4_host(_np_ptr(codes), _np_ptr(scales), K, N, layout, _np_ptr(out)),
+           "frt_weight_pack_mxfp4_host")
+    return out
+
+
+def frt_weight_unpack_mxfp4_host(packed, K, N, layout=W_PLAIN):
+    """Packed MXFP4 bytes -> (codes [K][N], scale bytes [K/32][N])."""
+    import numpy as np
+    packed = np.ascontiguousarray(packed).view(np.uint8)
+    codes = np.zeros((K, N), np.uint8)
+    scales = np.zeros((K // 32, N), np.uint8)
+    _check(_lib().frt_weight_unpack_mxfp4_host(_np_ptr(packed), K, N, layout, _np_ptr(codes), _np_ptr(scales)),
+           "frt_weight_unpack_mxfp4_host")
+    return codes, scales
 
 
 # ------------------------------------------------------------------ device entry points

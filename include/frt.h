@@ -62,7 +62,10 @@ typedef enum {
   FRT_E_ARG = 10        /* another invalid argument (epilogue, layout, eps, scale)      */
 } frt_status;
 
-typedef enum { FRT_BF16 = 1, FRT_E4M3 = 2, FRT_F32 = 3 } frt_dtype;
+/* FRT_MXFP4 is a weight format only (OCP MX, FP4 E2M1 elements with one E8M0 scale per
+ * 32 consecutive k of a column: 4-bit weights, the notes' "next" precision step); a GEMM
+ * with MXFP4 weights takes an FRT_E4M3 operand.                                        */
+typedef enum { FRT_BF16 = 1, FRT_E4M3 = 2, FRT_F32 = 3, FRT_MXFP4 = 4 } frt_dtype;
 
 /* Logical column order of a packed weight.  FRT_W_GATE_UP pairs column tile i of the
  * gate half [0, N/2) with tile i of the up half [N/2, N) so that one workgroup holds
@@ -85,7 +88,8 @@ int frt_version(void);             /* 100 * major + minor                       
 /* ------------------------------------------------------------------ layouts */
 /* Bytes of a packed GEMM operand (A) holding M x K values: Mp * K * (2 | 1). */
 size_t frt_operand_bytes(int dtype, int M, int K);
-/* Bytes of a packed weight holding K x N values: K * N * (2 | 1). */
+/* Bytes of a packed weight holding K x N values: K * N * (2 | 1), or for FRT_MXFP4
+ * K * N / 2 code bytes + K * N / 32 scale bytes (0 unless K % 128 == 0).             */
 size_t frt_weight_bytes(int dtype, int K, int N);
 
 /* Host-only layout helpers (no HIP call; used to inspect and build test data).
@@ -97,6 +101,12 @@ int frt_weight_pack_host(const void* codes_host, int dtype, int K, int N, int la
                          void* packed_host);
 int frt_weight_unpack_host(const void* packed_host, int dtype, int K, int N, int layout,
                            void* codes_host);
+/* FRT_MXFP4 weights: codes [K][N] one FP4 E2M1 code per byte (low 4 bits), scale bytes
+ * [K/32][N] E8M0 (block b covers k in [32b, 32b+32)).  K % 128 == 0.                  */
+int frt_weight_pack_mxfp4_host(const uint8_t* codes_host, const uint8_t* scales_host, int K, int N,
+                               int layout, void* packed_host);
+int frt_weight_unpack_mxfp4_host(const void* packed_host, int K, int N, int layout,
+                                 uint8_t* codes_host, uint8_t* scales_host);
 
 /* ------------------------------------------------------------------ offline weight prep */
 /* Pack a bf16 weight W [K][N] (row-major bits, device) for the skinny GEMM.
@@ -108,6 +118,12 @@ int frt_weight_unpack_host(const void* packed_host, int dtype, int K, int N, int
  *   colscale_dev [N] (fp32); codes e4m3(W'[k][n] / s_w[n]); a zero column gets s_w = 0
  *   and zero codes (the notes' static-quantisation section keeps weight scales apart
  *   from activation scales).
+ * dtype FRT_MXFP4: each block of 32 consecutive k of a column (k in [32b, 32b+32)) gets
+ *   the E8M0 scale X = 2^e, e = floor(log2 max|W'|) - 2 (the largest FP4 E2M1 magnitude
+ *   is 6 = 1.5 * 2^2), clamped to [-127, 127]; elements are FP4 E2M1 codes of W' / X,
+ *   rounded to nearest even and saturated at +-6; an all-zero block gets scale byte 0
+ *   and zero codes (OCP Microscaling Formats v1.0: MXFP4).  No column scale (colscale_dev
+ *   ignored); K % 128 == 0.
  * layout: FRT_W_PLAIN or FRT_W_GATE_UP (N % 32 == 0).  w_packed_dev must hold
  * frt_weight_bytes(dtype, K, N) bytes and must not overlap w_bf16_dev.              */
 int frt_pack_weight(void* stream, int K, int N, const uint16_t* w_bf16_dev,
@@ -139,7 +155,8 @@ int frt_residual_norm_quant(void* stream, int M, int K,
 
 /* ------------------------------------------------------------------ skinny GEMM */
 /* C = A W with A the packed operand [Mp][K] and W the packed weight [K][N], both
- * FRT_BF16 or both FRT_E4M3, MFMA with fp32 accumulation.  K is cut into `splits`
+ * FRT_BF16 or both FRT_E4M3, or (ab_dtype FRT_MXFP4) MXFP4 weights with an FRT_E4M3
+ * operand (block-scaled FP4 x FP8 MFMA), all with fp32 accumulation.  K is cut into `splits`
  * contiguous equal chunks; chunk j's product is partial P_j (notes, split-K equation).
  *
  * splits: 1, 2, 4, 8 or 16, or 0 to let the library choose for (M, N, K, dtype).
@@ -226,7 +243,8 @@ int frt_attention_prefix(void* stream, int M, int n_heads, int head_dim, int kv_
  * next input: notes, static-quantisation section).                                   */
 typedef struct frt_chain_desc {
   int layers, steps, M, hidden, n_heads, head_dim, prefix_len, mlp;
-  int dtype;                 /* FRT_BF16 or FRT_E4M3 (weights and GEMM inputs)          */
+  int dtype;                 /* FRT_BF16 or FRT_E4M3 (weights and GEMM inputs), or
+                                FRT_MXFP4 (MXFP4 weights, FRT_E4M3 GEMM inputs)         */
   float eps;
   int splits_qkv, splits_o, splits_up, splits_down;   /* 0 = library choice            */
   int use_graph;             /* 1: capture once, replay with one hipGraphLaunch          */

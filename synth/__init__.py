@@ -56,6 +56,15 @@ def weight_bf16(seed, workload, tensor, K, N):
     return to_bf16_bits(normal(seed, workload, tensor, (K, N), std=1.0 / np.sqrt(K)))
 
 
+def weight_bf16_block_spread(seed, workload, tensor, K, N, spread=6, block=32):
+    """W [K][N] ~ N(0, 1/K) times 2**e, one e uniform in [-spread, spread] per `block`
+    consecutive k of a column (bf16 bits).  Per-block magnitudes that differ by up to
+    2**(2*spread) make any mix-up between blocks and their scales visible."""
+    w = normal(seed, workload, tensor, (K, N), std=1.0 / np.sqrt(K))
+    e = rng(seed, workload, tensor + 1).integers(-spread, spread + 1, size=(K // block, N))
+    return to_bf16_bits(w * np.repeat(np.exp2(e), block, axis=0).astype(np.float32))
+
+
 def modulation(seed, workload, tensor, H, n=3):
     """[n][H] float32 conditioning outputs = c W_ada with c ~ N(0,1)^H, W_ada ~ N(0,1/H).
 

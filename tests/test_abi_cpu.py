@@ -101,6 +101,47 @@ def test_weight_layout_is_a_bijection(dtype, K, N, layout):
     assert np.array_equal(frt.frt_weight_unpack_host(packed, dtype, K, N, layout), codes)
 
 
+@pytest.mark.parametrize("K,N,layout", [(128, 16, frt.W_PLAIN), (512, 96, frt.W_PLAIN), (256, 64, frt.W_GATE_UP)])
+def test_mxfp4_weight_layout_is_a_bijection(K, N, layout):
+    g = np.random.default_rng(K + N)
+    codes = g.integers(0, 16, (K, N)).astype(np.uint8)
+    scales = g.integers(0, 255, (K // 32, N)).astype(np.uint8)
+    packed = frt.frt_weight_pack_mxfp4_host(codes, scales, K, N, layout)
+    assert packed.size == frt.frt_weight_bytes(frt.MXFP4, K, N) == K * N // 2 + K * N // 32
+    c2, s2 = frt.frt_weight_unpack_mxfp4_host(packed, K, N, layout)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+    # every code nibble and every scale byte has its own place: an all-ones pattern fills
+    # every byte of the packed weight
+    full = frt.frt_weight_pack_mxfp4_host(np.full((K, N), 15, np.uint8), np.full((K // 32, N), 255, np.uint8),
+                                          K, N, layout)
+    assert np.all(full == 255)
+
+
+def test_mxfp4_tile_structure():
+    """Tile (column tile, k-step) = 1 KB of codes then 64 scale bytes; lane L = column L%16,
+    MX block L/16 of the k-step: 32 consecutive k, two per byte, the even k in the low nibble."""
+    K, N = 256, 32
+    codes = ((np.arange(K)[:, None] + 3 * np.arange(N)[None, :]) % 16).astype(np.uint8)
+    scales = (np.arange(K // 32)[:, None] * 40 + np.arange(N)[None, :]).astype(np.uint8)
+    p = frt.frt_weight_pack_mxfp4_host(codes, scales, K, N, frt.W_PLAIN)
+    tiles = p.reshape(-1, 1088)                      # (column tile, k-step) order, k-step fastest
+    assert tiles.shape[0] == (N // 16) * (K // 128)
+    t = tiles[1]                                     # column tile 0, k-step 1 (k 128..255)
+    lane = 16 * 2 + 5                                # column 5, block 2 of the k-step: k 192..223
+    slot = t[lane * 16:lane * 16 + 16]
+    assert np.array_equal(slot & 15, codes[192:224:2, 5]) and np.array_equal(slot >> 4, codes[193:224:2, 5])
+    assert t[1024 + lane] == scales[6, 5]            # block 6 of the column = k 192..223
+    assert tiles[2][1024 + 3] == scales[0, 19]       # column tile 1, k-step 0, lane 3: column 19
+
+
+def test_mxfp4_rejected_where_only_operand_formats_belong():
+    assert frt.frt_operand_bytes(frt.MXFP4, 10, 1024) == 0
+    assert frt.frt_weight_bytes(frt.MXFP4, 96, 64) == 0          # K must be a multiple of 128
+    with pytest.raises(frt.FrtError):
+        frt.frt_weight_pack_host(np.zeros((128, 16), np.uint8), frt.MXFP4, 128, 16)
+    assert frt.frt_splitk_choose(50, 16384, 2048, frt.MXFP4) == frt.frt_splitk_choose(50, 16384, 2048, frt.E4M3)
+
+
 def test_gate_up_layout_pairs_column_tiles():
     K, N = 32, 64
     codes = np.tile(np.arange(N, dtype=np.uint16), (K, 1))

@@ -44,6 +44,9 @@ def _oracle_weights(layers, dtype):
     for lw in layers:
         d = {}
         for name in ("qkv", "o", "up", "down"):
+            if dtype == "mxfp4":
+                d[name] = ref.pack_weight_mxfp4(codec.bf16_decode(lw[name]))[2]
+                continue
             codes, s_w, _ = ref.pack_weight_values(codec.bf16_decode(lw[name]), None, dtype)
             d[name] = codec.decode(codes, dtype)
             if s_w is not None:
@@ -61,13 +64,17 @@ def _oracle_run(wl, ws, scales, dtype, trace=None, perturb=None):
 
 
 @pytest.mark.parametrize("dtype,M,splits", [("bf16", 50, (0, 0, 0, 0)), ("e4m3", 50, (0, 0, 0, 0)),
-                                            ("bf16", 10, (2, 1, 2, 8)), ("e4m3", 10, (1, 2, 1, 4))])
+                                            ("bf16", 10, (2, 1, 2, 8)), ("e4m3", 10, (1, 2, 1, 4)),
+                                            ("mxfp4", 50, (0, 0, 0, 0)), ("mxfp4", 10, (1, 2, 1, 4))])
 def test_chain_parity(F, dtype, M, splits):
     frt, chain = F
     dims = synth.chain_dims(layers=2, steps=2, M=M)
     wl = synth.workload4(dims)
-    dt = frt.DTYPES[dtype]
+    wdt = frt.DTYPES[dtype]
     ws = _oracle_weights(wl["layers"], dtype)
+    # MXFP4 weights multiply e4m3 activations: the activation side is the e4m3 chain's
+    dtype = "e4m3" if dtype == "mxfp4" else dtype
+    dt = frt.DTYPES[dtype]
     scales = None
     if dtype == "e4m3":
         x0c, modc = synth.chain_inputs(dims, synth.CAL_SEED)
@@ -82,14 +89,14 @@ def test_chain_parity(F, dtype, M, splits):
                               perturb=lambda v: v * (1.0 + noise * g.standard_normal(v.shape))), want)
     bar = mult * max(sens, 1e-6 / mult)
 
-    packed = chain.PackedLayers(wl["layers"], dims, dt)
+    packed = chain.PackedLayers(wl["layers"], dims, wdt)
     cg = chain.Chain(dims, packed, splits=splits, use_graph=True, keep_intermediates=True)
     chain.load_workload(cg, wl, scales)
     cg.run()
     torch.cuda.synchronize()
     got = cg.read("x_out").reshape(M, -1)
     err = rel_l2(got, want)
-    print(f"chain {dtype} M={M}: rel L2 {err:.3e}, oracle sensitivity {sens:.3e}, bar {bar:.3e}, "
+    print(f"chain weights {wdt} acts {dtype} M={M}: rel L2 {err:.3e}, oracle sensitivity {sens:.3e}, bar {bar:.3e}, "
           f"kernels {cg.kernel_count()}")
     assert err <= bar
     # the first GEMM input depends on the chain inputs only: codes exact up to the tie band
