@@ -119,6 +119,9 @@ static GemmShape choose_shape(const GemmParams& p) {
   const int run = kps / sh.kw;
   sh.per = per_max(p.ab_dtype, sh.nt, sh.mbw);
   while (sh.per > 1 && run % sh.per) sh.per /= 2;
+  const bool scaled = sh.epi != kGemmPartial &&
+                      (p.act_scale_ptr || p.colscale || p.out_scale_ptr || p.amax);
+  sh.fast = sh.kw == 4 && run == sh.per && !scaled;
   return sh;
 }
 
