@@ -121,7 +121,7 @@ static GemmShape choose_shape(const GemmParams& p) {
   while (sh.per > 1 && run % sh.per) sh.per /= 2;
   const bool scaled = sh.epi != kGemmPartial &&
                       (p.act_scale_ptr || p.colscale || p.out_scale_ptr || p.amax);
-  sh.fast = sh.kw == 4 && run == sh.per && !scaled;
+  sh.fast = sh.kw == 4 && run == sh.per ? (scaled ? kFastShape : kFastPlain) : kGeneric;
   return sh;
 }
 

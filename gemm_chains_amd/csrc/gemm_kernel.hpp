@@ -25,11 +25,13 @@ enum GemmEpi { kGemmPartial = 0, kGemmStore = 1, kGemmSiluBf16 = 2, kGemmSiluE4m
 
 // Tile shape of a launch: NT column tiles and MB row blocks per workgroup, kw waves with
 // PER k-steps per round; (col_groups x row_groups) workgroups per split.  `fast` selects
-// the kernel specialised for the common case: four waves, one round each, and no scale
-// read through a pointer (no column scales, no calibration maxima).
+// a kernel specialised for the common cases: kFastShape = four waves with one round each;
+// kFastPlain = that and no scale read through a pointer (no column scales, no calibration
+// maxima).
+enum GemmFast { kGeneric = 0, kFastShape = 1, kFastPlain = 2 };
 struct GemmShape {
   int nt, mbw, per, kw, col_groups, row_groups, epi;
-  bool fast;
+  int fast;
 };
 
 template <int DT>
@@ -117,10 +119,12 @@ __device__ __forceinline__ float silu_f(float g) {
 // the row grouping.  Row groups (XCD-aware: the groups that share a column group are
 // eight workgroup ids apart, so they run on one XCD and its L2 serves the weight tile
 // to all of them after one HBM read) spread GEMMs with few column tiles over more CUs.
-// FAST fixes four waves and a single round and drops the pointer-read scales: measured
-// on MI355X, the shorter, branch-free code saves 0.4 us per launch of the gate|up GEMM.
-template <int DT, int MB, int NT, int PER, int EPI, bool FAST>
+// FAST (GemmFast) fixes four waves and a single round, and with kFastPlain drops the
+// pointer-read scales: measured on MI355X, the shorter, branch-free code saves 0.4 us per
+// launch of the gate|up GEMM.
+template <int DT, int MB, int NT, int PER, int EPI, int FAST>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
+  constexpr bool SHAPE = FAST != kGeneric, PLAIN = FAST == kFastPlain;
   constexpr int ADT = act_dtype_of(DT);   // operand (activation) format
   constexpr int TBW = tile_bytes_of(DT);  // weight tile bytes
   constexpr int TB = tile_bytes_of(ADT);  // operand tile bytes
@@ -131,7 +135,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
   // wave index made provably uniform: MFMAs ignore EXEC, so every branch around them must
   // be a scalar branch, never an EXEC-masked one
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kw = FAST ? 4 : p.kwaves;
+  const int kw = SHAPE ? 4 : p.kwaves;
   const int KS = p.ksteps;
   const int run = p.run;  // = PER * rounds
   // grid: (col_groups, 1, splits), or with row groups (8 * row_groups, ceil(col_groups / 8),
@@ -179,11 +183,11 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) acc[t][b] = mma(wf[u][t], af[u][b], acc[t][b]);
     ks0 += PER;
-  } while (!FAST && ks0 < ks_begin + run);
+  } while (!SHAPE && ks0 < ks_begin + run);
   if (!active) return;  // whole workgroup
 
   // ---- epilogue (one per kernel)
-  const float as = FAST ? p.act_scale : load_scale(p.act_scale_ptr, p.act_scale);
+  const float as = PLAIN ? p.act_scale : load_scale(p.act_scale_ptr, p.act_scale);
   // fragment (t, b) finished: partial store, or scale recovery + store / Q-K-V scatter
   auto finish = [&](int t, int b, f32x4 v) {
     const int n0 = logical_tile_of(p.layout, p.N, g * NT + t) * 16 + 4 * (lane >> 4);
@@ -193,7 +197,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
       *reinterpret_cast<f32x4*>(p.partials + ((size_t)split * p.M + m) * p.N + n0) = v;
     } else {
       f32x4 c = v * as;
-      if (!FAST && p.colscale) c *= *reinterpret_cast<const f32x4*>(p.colscale + n0);
+      if (!PLAIN && p.colscale) c *= *reinterpret_cast<const f32x4*>(p.colscale + n0);
       if constexpr (EPI == kGemmQkv) {
         store_qkv4(p.q_out, p.k_out, p.v_out, p.nq, p.hd, p.v_ld, m, n0, c);
       } else if (p.epi == FRT_EPI_STORE_F32) {
@@ -213,17 +217,17 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
     const int nu = logical_tile_of(p.layout, p.N, g * NT + 2 * tp + 1) * 16 + 4 * (lane >> 4);
     const int m = (mb0 + b) * 16 + (lane & 15);
     f32x4 cg = vg * as, cu = vu * as;
-    if (!FAST && p.colscale) {
+    if (!PLAIN && p.colscale) {
       cg *= *reinterpret_cast<const f32x4*>(p.colscale + ng);
       cu *= *reinterpret_cast<const f32x4*>(p.colscale + nu);
     }
     float z[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) z[e] = silu_f(cg[e]) * cu[e];
-    const float os = FAST ? p.out_scale : load_scale(p.out_scale_ptr, p.out_scale);
+    const float os = PLAIN ? p.out_scale : load_scale(p.out_scale_ptr, p.out_scale);
     store_operand4(reinterpret_cast<uint8_t*>(p.out), EPI == kGemmSiluBf16 ? FRT_BF16 : FRT_E4M3, p.MB, m, ng,
                    z[0], z[1], z[2], z[3], os, m >= p.M);
-    if (!FAST && m < p.M) record_amax(p.amax, z[0], z[1], z[2], z[3]);
+    if (!PLAIN && m < p.M) record_amax(p.amax, z[0], z[1], z[2], z[3]);
   };
 
   // combine the kw (<= 4) waves' sums in wave order through LDS (with one wave too: a
@@ -261,8 +265,12 @@ static hipError_t launch_t(const GemmParams& p, const GemmShape& sh, hipStream_t
     const dim3 grid = sh.row_groups == 1 ? dim3(sh.col_groups, 1, p.splits)
                                          : dim3(8 * sh.row_groups, (sh.col_groups + 7) / 8, p.splits);
     const size_t lds = (size_t)p.kwaves * NT * MB * 64 * sizeof(f32x4);
-    if (sh.fast) hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, true>), grid, dim3(256), lds, s, p);
-    else hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, false>), grid, dim3(64 * p.kwaves), lds, s, p);
+    if (sh.fast == kFastPlain)
+      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastPlain>), grid, dim3(256), lds, s, p);
+    else if (sh.fast == kFastShape)
+      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastShape>), grid, dim3(256), lds, s, p);
+    else
+      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kGeneric>), grid, dim3(64 * p.kwaves), lds, s, p);
     return hipGetLastError();
   }
 }
