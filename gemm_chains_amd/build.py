@@ -9,7 +9,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfrt.so")
-SOURCES = ["api.hip", "pack.hip", "rnq.hip", "gemm.hip", "gemm_bf16.hip", "gemm_e4m3.hip", "gemm_mxfp4.hip", "attn.hip", "chain.hip"]
+SOURCES = ["api.hip", "pack.hip", "rnq.hip", "gemm.hip", "gemm_bf16.hip", "gemm_bf16_silu.hip", "gemm_e4m3.hip",
+           "gemm_e4m3_silu.hip", "gemm_mxfp4.hip", "gemm_mxfp4_silu.hip", "attn.hip", "chain.hip"]
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-function",
          # packed-FP32 VALU forms are kept out of every kernel (device-only target feature)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

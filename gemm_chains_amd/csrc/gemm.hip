@@ -141,6 +141,29 @@ WeightTouch gemm_weight_touch(const GemmParams& p, int part, int parts) {
   return t;
 }
 
+// The kernels are compiled in the gemm_{bf16,e4m3,mxfp4}{,_silu}.hip units, not here.
+#define FRT_GEMM_EXTERN(DT)                                                                              \
+  extern template hipError_t launch_gemm_epi<DT, kGemmPartial>(const GemmParams&, const GemmShape&, hipStream_t); \
+  extern template hipError_t launch_gemm_epi<DT, kGemmStore>(const GemmParams&, const GemmShape&, hipStream_t);   \
+  extern template hipError_t launch_gemm_epi<DT, kGemmQkv>(const GemmParams&, const GemmShape&, hipStream_t);     \
+  extern template hipError_t launch_gemm_epi<DT, kGemmSiluBf16>(const GemmParams&, const GemmShape&, hipStream_t); \
+  extern template hipError_t launch_gemm_epi<DT, kGemmSiluE4m3>(const GemmParams&, const GemmShape&, hipStream_t);
+FRT_GEMM_EXTERN(FRT_BF16)
+FRT_GEMM_EXTERN(FRT_E4M3)
+FRT_GEMM_EXTERN(FRT_MXFP4)
+#undef FRT_GEMM_EXTERN
+
+template <int DT>
+static hipError_t launch_gemm_dt(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
+  switch (sh.epi) {
+    case kGemmPartial: return launch_gemm_epi<DT, kGemmPartial>(p, sh, s);
+    case kGemmStore: return launch_gemm_epi<DT, kGemmStore>(p, sh, s);
+    case kGemmSiluBf16: return launch_gemm_epi<DT, kGemmSiluBf16>(p, sh, s);
+    case kGemmSiluE4m3: return launch_gemm_epi<DT, kGemmSiluE4m3>(p, sh, s);
+    default: return launch_gemm_epi<DT, kGemmQkv>(p, sh, s);
+  }
+}
+
 hipError_t launch_gemm(const GemmParams& p_in, hipStream_t s) {
   GemmParams p = p_in;
   const GemmShape sh = choose_shape(p);
@@ -150,9 +173,9 @@ hipError_t launch_gemm(const GemmParams& p_in, hipStream_t s) {
   p.row_groups = sh.row_groups;
   p.col_groups = sh.col_groups;
   switch (p.ab_dtype) {
-    case FRT_BF16: return launch_gemm_typed<FRT_BF16>(p, sh, s);
-    case FRT_E4M3: return launch_gemm_typed<FRT_E4M3>(p, sh, s);
-    default: return launch_gemm_typed<FRT_MXFP4>(p, sh, s);
+    case FRT_BF16: return launch_gemm_dt<FRT_BF16>(p, sh, s);
+    case FRT_E4M3: return launch_gemm_dt<FRT_E4M3>(p, sh, s);
+    default: return launch_gemm_dt<FRT_MXFP4>(p, sh, s);
   }
 }
 

@@ -1,0 +1,8 @@
+// Skinny split-K GEMM kernels with bf16 weights and operands: SiLU-gate epilogues with a bf16
+// or e4m3 output operand.
+#include "gemm_kernel.hpp"
+
+namespace frt {
+template hipError_t launch_gemm_epi<FRT_BF16, kGemmSiluBf16>(const GemmParams&, const GemmShape&, hipStream_t);
+template hipError_t launch_gemm_epi<FRT_BF16, kGemmSiluE4m3>(const GemmParams&, const GemmShape&, hipStream_t);
+}  // namespace frt

@@ -1,5 +1,5 @@
-// Skinny split-K GEMM kernel template (instantiated per weight format in gemm_bf16.hip,
-// gemm_e4m3.hip and gemm_mxfp4.hip; host side in gemm.hip).
+// Skinny split-K GEMM kernel template (instantiated per weight format and epilogue in the
+// gemm_{bf16,e4m3,mxfp4}{,_silu}.hip translation units; host side in gemm.hip).
 //
 // Pages: observation-age notes ("思考探索：具身推理加速，先看动作执行时观测有多旧"),
 // section "小 M GEMM 要看并行度，也要看归约代价" (C = A W with few rows, cut along K into
@@ -275,43 +275,34 @@ static hipError_t launch_t(const GemmParams& p, const GemmShape& sh, hipStream_t
   }
 }
 
-template <int DT, int MB, int NT, int PER>
-static hipError_t launch_epi(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
-  switch (sh.epi) {
-    case kGemmPartial: return launch_t<DT, MB, NT, PER, kGemmPartial>(p, sh, s);
-    case kGemmStore: return launch_t<DT, MB, NT, PER, kGemmStore>(p, sh, s);
-    case kGemmSiluBf16: return launch_t<DT, MB, NT, PER, kGemmSiluBf16>(p, sh, s);
-    case kGemmSiluE4m3: return launch_t<DT, MB, NT, PER, kGemmSiluE4m3>(p, sh, s);
-    default: return launch_t<DT, MB, NT, PER, kGemmQkv>(p, sh, s);
-  }
-}
-
-template <int DT, int MB, int NT>
+template <int DT, int EPI, int MB, int NT>
 static hipError_t launch_per(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
   switch (sh.per) {
-    case 1: return launch_epi<DT, MB, NT, 1>(p, sh, s);
-    case 2: return launch_epi<DT, MB, NT, 2>(p, sh, s);
-    case 4: return launch_epi<DT, MB, NT, 4>(p, sh, s);
-    default: return launch_epi<DT, MB, NT, 8>(p, sh, s);
+    case 1: return launch_t<DT, MB, NT, 1, EPI>(p, sh, s);
+    case 2: return launch_t<DT, MB, NT, 2, EPI>(p, sh, s);
+    case 4: return launch_t<DT, MB, NT, 4, EPI>(p, sh, s);
+    default: return launch_t<DT, MB, NT, 8, EPI>(p, sh, s);
   }
 }
 
-template <int DT, int MB>
+template <int DT, int EPI, int MB>
 static hipError_t launch_nt(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
   switch (sh.nt) {
-    case 1: return launch_per<DT, MB, 1>(p, sh, s);
-    case 2: return launch_per<DT, MB, 2>(p, sh, s);
-    default: return launch_per<DT, MB, 4>(p, sh, s);
+    case 1: return launch_per<DT, EPI, MB, 1>(p, sh, s);
+    case 2: return launch_per<DT, EPI, MB, 2>(p, sh, s);
+    default: return launch_per<DT, EPI, MB, 4>(p, sh, s);
   }
 }
 
-template <int DT>
-hipError_t launch_gemm_typed(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
+// All kernels of one (weight format, epilogue); explicitly instantiated in the gemm_*.hip
+// translation units, a few per file, so that they compile in parallel.
+template <int DT, int EPI>
+hipError_t launch_gemm_epi(const GemmParams& p, const GemmShape& sh, hipStream_t s) {
   switch (sh.mbw) {
-    case 1: return launch_nt<DT, 1>(p, sh, s);
-    case 2: return launch_nt<DT, 2>(p, sh, s);
-    case 3: return launch_nt<DT, 3>(p, sh, s);
-    default: return launch_nt<DT, 4>(p, sh, s);
+    case 1: return launch_nt<DT, EPI, 1>(p, sh, s);
+    case 2: return launch_nt<DT, EPI, 2>(p, sh, s);
+    case 3: return launch_nt<DT, EPI, 3>(p, sh, s);
+    default: return launch_nt<DT, EPI, 4>(p, sh, s);
   }
 }
 
