@@ -52,6 +52,39 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
   const size_t row = (size_t)m * K;
   const size_t split_stride = (size_t)p.M * K;
 
+  // Every input of the row is requested before the first one is used: the partials, the
+  // residual, the per-channel vectors and the scalar scales.  (Loads behind a null test
+  // would each wait for the data before them, and loads after the barrier below would
+  // cost one more memory round trip each.)  A missing vector reads the residual's row
+  // in its place, which is always valid, and its value is then not used.
+  const bool has_cs = p.x_colscale != nullptr, has_gate = p.gate != nullptr;
+  const bool has_as = p.ada_scale != nullptr, has_sh = p.ada_shift != nullptr;
+  const float* csp = has_cs ? p.x_colscale : p.residual;
+  const float* gtp = has_gate ? p.gate : p.residual;
+  const float* asp = has_as ? p.ada_scale : p.residual;
+  const float* shp = has_sh ? p.ada_shift : p.residual;
+  const float xs = SPL != 0 ? load_scale(p.x_scale_ptr, p.x_scale) : 1.f;
+  const float as = load_scale(p.act_scale_ptr, p.act_scale);
+  f32x4 r[G], xp[G][SPL > 0 ? SPL : 1], cs[G], gt[G], av[G], sv[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int k0 = 4 * (tid + 256 * i);
+    if (k0 >= K) continue;
+    r[i] = *reinterpret_cast<const f32x4*>(p.residual + row + k0);
+    if constexpr (SPL > 0) {
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) xp[i][j] = *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
+    }
+    if constexpr (SPL != 0) {
+      cs[i] = *reinterpret_cast<const f32x4*>(csp + k0);
+      gt[i] = *reinterpret_cast<const f32x4*>(gtp + k0);
+    }
+    if constexpr (ODT != 0) {
+      av[i] = *reinterpret_cast<const f32x4*>(asp + k0);
+      sv[i] = *reinterpret_cast<const f32x4*>(shp + k0);
+    }
+  }
+
   f32x4 h[G];
   float ss = 0.f;
 #pragma unroll
@@ -61,25 +94,21 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
       h[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       continue;
     }
-    const f32x4 r = *reinterpret_cast<const f32x4*>(p.residual + row + k0);
-    f32x4 hv = r;
+    f32x4 hv = r[i];
     if constexpr (SPL != 0) {
       f32x4 x;
       if constexpr (SPL > 0) {
-        f32x4 xp[SPL];
+        x = xp[i][0];
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) xp[j] = *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
-        x = xp[0];
-#pragma unroll
-        for (int j = 1; j < SPL; ++j) x += xp[j];  // partials summed in ascending split order
+        for (int j = 1; j < SPL; ++j) x += xp[i][j];  // partials summed in ascending split order
       } else {
         x = *reinterpret_cast<const f32x4*>(p.x + row + k0);
         for (int j = 1; j < p.x_splits; ++j) x += *reinterpret_cast<const f32x4*>(p.x + j * split_stride + row + k0);
       }
-      x *= load_scale(p.x_scale_ptr, p.x_scale);  // then scale recovery
-      if (p.x_colscale) x *= *reinterpret_cast<const f32x4*>(p.x_colscale + k0);
-      if (p.gate) x *= *reinterpret_cast<const f32x4*>(p.gate + k0);
-      hv = r + x;
+      x *= xs;  // then scale recovery
+      if (has_cs) x *= cs[i];
+      if (has_gate) x *= gt[i];
+      hv = hv + x;
     }
     h[i] = hv;
 #pragma unroll
@@ -99,14 +128,13 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
     __syncthreads();
     const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
     const float inv = 1.0f / sqrtf(tot / (float)K + p.eps);
-    const float as = load_scale(p.act_scale_ptr, p.act_scale);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const int k0 = 4 * (tid + 256 * i);
       if (k0 >= K) continue;
       f32x4 y = h[i] * inv;
-      if (p.ada_scale) y = y * (1.0f + *reinterpret_cast<const f32x4*>(p.ada_scale + k0));
-      if (p.ada_shift) y = y + *reinterpret_cast<const f32x4*>(p.ada_shift + k0);
+      if (has_as) y = y * (1.0f + av[i]);
+      if (has_sh) y = y + sv[i];
       store_operand4(p.operand, ODT, p.MB, m, k0, y.x, y.y, y.z, y.w, as, false);
       record_amax(p.amax, y.x, y.y, y.z, y.w);
     }
