@@ -186,7 +186,7 @@ def gemm_sweep(torch, frt, device, synth):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gate_up_gemm_bf16_m50_hbm_traffic.md")
 GEMM_SOURCES = [os.path.join(ROOT, "gemm_chains_amd", "csrc", f)
-                for f in ("gemm.hip", "gemm_kernel.hpp", "gemm_bf16.hip", "frt_internal.hpp")]
+                for f in ("gemm.hip", "gemm_kernel.hpp", "gemm_bf16_silu.hip", "frt_internal.hpp")]
 
 
 def measured_traffic():
