@@ -32,24 +32,27 @@ __device__ __forceinline__ bf16x8 bf16x8_from(const uint32_t* w4) {
 // [chunks][heads][MB] partial records of (16 m | 16 l | 16*128 O) fp32.
 __host__ __device__ inline size_t attn_record_floats() { return 32 + 16 * HD; }
 
-// Keys per workgroup.  Measured on MI355X (M = 50, 850 keys): one 32-key block per wave
-// in 128-key chunks of 4 waves, merged by a second kernel, beats whole-sequence
-// workgroups whose waves walk several blocks in turn (each block then pays its own load
-// latency, and one CU fetches every key and value line of the sequence).  A sequence of
-// at most 128 keys needs no merge.  FRT_ATTN_CHUNK_KEYS (128, 256, 512 or 1024)
-// overrides the choice for tuning; chunks of 256 and more use 8 waves.
-int attention_chunk_keys(int kv_len) {
+// Keys per workgroup.  Measured on MI355X (850 keys): one 32-key block per wave, merged
+// by a second kernel, beats whole-sequence workgroups whose waves walk several blocks in
+// turn (each block then pays its own load latency, and one CU fetches every key and value
+// line of the sequence).  128-key chunks of 4 waves are fastest while they give at least
+// 128 workgroups (M = 50: 34.5 us/layer against 36.1 with 64-key chunks); below that,
+// 64-key chunks of 2 waves spread the work wider (M = 10: 29.6 against 30.2).  A
+// sequence that fits one chunk needs no merge.  FRT_ATTN_CHUNK_KEYS (64, 128, 256, 512 or
+// 1024) overrides the choice for tuning; chunks of 256 and more use 8 waves.
+int attention_chunk_keys(int M, int n_heads, int kv_len) {
   static int env = -1;
   if (env < 0) {
     const char* e = getenv("FRT_ATTN_CHUNK_KEYS");
     env = e ? atoi(e) : 0;
-    if (env != 128 && env != 256 && env != 512 && env != 1024) env = 0;
+    if (env != 64 && env != 128 && env != 256 && env != 512 && env != 1024) env = 0;
   }
-  (void)kv_len;
-  return env > 0 ? env : 128;
+  if (env > 0) return env;
+  const int wgs128 = n_heads * ((M + 15) / 16) * ((kv_len + 127) / 128);
+  return wgs128 < 128 && kv_len > 64 ? 64 : 128;
 }
 size_t attention_workspace_bytes(int M, int n_heads, int kv_len) {
-  const int MB = (M + 15) / 16, ck = attention_chunk_keys(kv_len), nch = (kv_len + ck - 1) / ck;
+  const int MB = (M + 15) / 16, ck = attention_chunk_keys(M, n_heads, kv_len), nch = (kv_len + ck - 1) / ck;
   return nch > 1 ? (size_t)nch * n_heads * MB * attn_record_floats() * 4 : 16;
 }
 
@@ -327,11 +330,12 @@ static void launch_combine(const AttnParams& p, int nch, hipStream_t s) {
 
 hipError_t launch_attention(const AttnParams& p_in, hipStream_t s) {
   AttnParams p = p_in;
-  p.chunk_keys = attention_chunk_keys(p.kv_len);
+  p.chunk_keys = attention_chunk_keys(p.M, p.n_heads, p.kv_len);
   const int nch = (p.kv_len + p.chunk_keys - 1) / p.chunk_keys;
   const dim3 g(p.n_heads, p.MB, nch);
   const bool rec = nch > 1;
-  if (p.chunk_keys <= 128) rec ? launch_chunk<4, false, true>(p, g, s) : launch_chunk<4, false, false>(p, g, s);
+  if (p.chunk_keys <= 64) rec ? launch_chunk<2, false, true>(p, g, s) : launch_chunk<2, false, false>(p, g, s);
+  else if (p.chunk_keys <= 128) rec ? launch_chunk<4, false, true>(p, g, s) : launch_chunk<4, false, false>(p, g, s);
   else if (p.chunk_keys <= 256) rec ? launch_chunk<8, false, true>(p, g, s) : launch_chunk<8, false, false>(p, g, s);
   else rec ? launch_chunk<8, true, true>(p, g, s) : launch_chunk<8, true, false>(p, g, s);
   hipError_t e = hipGetLastError();
@@ -342,8 +346,8 @@ hipError_t launch_attention(const AttnParams& p_in, hipStream_t s) {
   return hipGetLastError();
 }
 
-int attention_kernel_count(int kv_len) {
-  const int ck = attention_chunk_keys(kv_len);
+int attention_kernel_count(int M, int n_heads, int kv_len) {
+  const int ck = attention_chunk_keys(M, n_heads, kv_len);
   return (kv_len + ck - 1) / ck > 1 ? 2 : 1;
 }
 

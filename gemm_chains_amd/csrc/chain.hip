@@ -271,7 +271,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
       t.out_dtype = adt; t.out_scale = 1.f; t.out_scale_ptr = actp(l, SITE_O);
       t.operand = a_o; t.workspace = (float*)at(c, L.aws);
       t.amax = amax ? amax + l * 4 + SITE_O : nullptr;
-      FRT_HIP(launch_attention(t, s)); n += attention_kernel_count(L.kv_len);
+      FRT_HIP(launch_attention(t, s)); n += attention_kernel_count(M, d.n_heads, L.kv_len);
 
       // 4. O projection -> partials
       FRT_HIP(launch_gemm(go, s)); ++n;
@@ -397,7 +397,7 @@ extern "C" int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_de
     c->kernels = n;
   } else {
     // count the launches without enqueueing anything
-    const int per_layer = 6 + attention_kernel_count(c->L.kv_len) + (c->L.s_up > 1) + (c->L.s_qkv > 1);
+    const int per_layer = 6 + attention_kernel_count(c->d.M, c->d.n_heads, c->L.kv_len) + (c->L.s_up > 1) + (c->L.s_qkv > 1);
     c->kernels = desc->steps * desc->layers * per_layer + 1;
   }
   *out = c;

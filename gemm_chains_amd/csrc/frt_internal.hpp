@@ -383,7 +383,7 @@ struct AttnParams {
 constexpr int kEpiQkv = 4;   // reduce + scale recovery + bf16, scattered into Q / K / V rows
 
 size_t attention_workspace_bytes(int M, int n_heads, int kv_len);
-int attention_kernel_count(int kv_len);
+int attention_kernel_count(int M, int n_heads, int kv_len);
 
 // Launchers (stream-ordered, no validation: callers validate first).
 hipError_t launch_rnq(const RnqParams& p, hipStream_t s);

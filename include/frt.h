@@ -215,7 +215,8 @@ int frt_skinny_gemm_qkv(void* stream, int M, int K, int n_heads, int head_dim, i
  *   O[m][h*d + e] = softmax_t(q_h . k_t / sqrt(d)) v_t[e], fp32-accurate;
  *   operand_out = packed bf16(O) or e4m3(O / out_act_scale), Mp x n_heads*head_dim.
  * Short sequences run as one workgroup per (head, 16-row block); long ones are cut into
- * 256-key chunks whose FP32 partials (max, sum, unnormalised output) a second kernel
+ * 128-key chunks (64-key chunks when that would leave fewer than 128 workgroups) whose
+ * FP32 partials (max, sum, unnormalised output) a second kernel
  * merges in chunk order (deterministic).
  * workspace_dev: frt_attention_workspace_bytes(...) bytes, no initial contents needed;
  * calls that share a workspace must not overlap in time.
