@@ -98,8 +98,10 @@ __device__ __forceinline__ void attend_block(const KVBlock& b, const bf16x8 (&qf
       s[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[dc], s[hf], 0, 0, 0);
     }
   }
-  // s[hf][r] = score of key t0 + 16*hf + 4*(L/16) + r for query L%16
-  const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+  // s[hf][r] = score of key t0 + 16*hf + 4*(L/16) + r for query L%16, kept in base-2
+  // units (scaled by log2(e) / sqrt(128)) so every exponential is one hardware exp2;
+  // maxima and the merge weights below use the same units
+  const float scale = 0.08838834764831845f * 1.4426950408889634f;
   float bmax = NEG_INF;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
@@ -111,14 +113,14 @@ __device__ __forceinline__ void attend_block(const KVBlock& b, const bf16x8 (&qf
   bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
   bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
   const float m_new = fmaxf(m_run, bmax);  // finite: the block holds a key < T
-  const float alpha = expf(m_run - m_new);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   float pr[8];
   float psum = 0.f;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pr[4 * hf + r] = expf(s[hf][r] - m_new);
+      pr[4 * hf + r] = __builtin_amdgcn_exp2f(s[hf][r] - m_new);
       psum += pr[4 * hf + r];
     }
   l_run = l_run * alpha + psum;
@@ -228,7 +230,7 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
   for (int w = 0; w < NW; ++w) mx = fmaxf(mx, cm[w][tq]);
   float wgt[NW], den = 0.f;
   for (int w = 0; w < NW; ++w) {
-    wgt[w] = cm[w][tq] == NEG_INF ? 0.f : expf(cm[w][tq] - mx);
+    wgt[w] = cm[w][tq] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(cm[w][tq] - mx);
     den += wgt[w] * cl[w][tq];
   }
   float* rec = p.workspace + (((size_t)ch * p.n_heads + h) * MB + mb) * attn_record_floats();
@@ -267,7 +269,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
   const size_t cstride = (size_t)p.n_heads * MB * attn_record_floats();
   float mx = NEG_INF, den = 0.f, num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto add = [&](float mc, float lc, f32x4 a, f32x4 b) {
-    const float wc = mc == NEG_INF ? 0.f : expf(mc - mx);
+    const float wc = mc == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mc - mx);  // base-2 maxima
     den += wc * lc;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
