@@ -242,7 +242,7 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
     f32x4 acc = comb[0][dt][lg * 16 + tq] * wgt[0];
     for (int w = 1; w < NW; ++w) acc += comb[w][dt][lg * 16 + tq] * wgt[w];
     if constexpr (!REC) {
-      const f32x4 ov = acc / den;
+      const f32x4 ov = acc * (1.0f / den);
       store_operand4(p.operand, ODT, MB, m, h * HD + d, ov.x, ov.y, ov.z, ov.w, os, m >= M);
       if (m < M) record_amax(p.amax, ov.x, ov.y, ov.z, ov.w);
     } else {
@@ -278,24 +278,25 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
     }
   };
   if constexpr (CH > 0) {
+    // slots past the last chunk load chunk 0 again (always valid) and weigh it 0, so
+    // every load is unconditional and all are issued together
     float mc[CH], lc[CH];
     f32x4 a[CH], b[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if (c < nch) {
-        const float* rc = rec0 + c * cstride;
-        mc[c] = rc[tq];
-        lc[c] = rc[16 + tq];
-        a[c] = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0);
-        b[c] = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0 + 4);
-      }
+      const float* rc = rec0 + (c < nch ? c : 0) * cstride;
+      mc[c] = rc[tq];
+      lc[c] = rc[16 + tq];
+      a[c] = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0);
+      b[c] = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0 + 4);
     }
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
-      if (c < nch) mx = fmaxf(mx, mc[c]);
+    for (int c = 0; c < CH; ++c) {
+      if (c >= nch) mc[c] = NEG_INF;
+      mx = fmaxf(mx, mc[c]);
+    }
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
-      if (c < nch) add(mc[c], lc[c], a[c], b[c]);
+    for (int c = 0; c < CH; ++c) add(mc[c], lc[c], a[c], b[c]);
   } else {
     for (int c = 0; c < nch; ++c) mx = fmaxf(mx, rec0[c * cstride + tq]);
     for (int c = 0; c < nch; ++c) {
@@ -307,12 +308,15 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
   const float os = load_scale(p.out_scale_ptr, p.out_scale);
   const int m = mb * 16 + tq;
   const int k = h * HD + d0;
-  store_operand4(p.operand, ODT, MB, m, k, num[0] / den, num[1] / den, num[2] / den, num[3] / den, os, m >= p.M);
-  store_operand4(p.operand, ODT, MB, m, k + 4, num[4] / den, num[5] / den, num[6] / den, num[7] / den, os,
-                 m >= p.M);
+  const float rden = 1.0f / den;  // one division; the products are within an ulp of the quotients
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = num[e] * rden;
+  store_operand4(p.operand, ODT, MB, m, k, o[0], o[1], o[2], o[3], os, m >= p.M);
+  store_operand4(p.operand, ODT, MB, m, k + 4, o[4], o[5], o[6], o[7], os, m >= p.M);
   if (m < p.M) {
-    record_amax(p.amax, num[0] / den, num[1] / den, num[2] / den, num[3] / den);
-    record_amax(p.amax, num[4] / den, num[5] / den, num[6] / den, num[7] / den);
+    record_amax(p.amax, o[0], o[1], o[2], o[3]);
+    record_amax(p.amax, o[4], o[5], o[6], o[7]);
   }
 }
 
