@@ -87,16 +87,15 @@ __device__ __forceinline__ void attend_block(const KVBlock& b, const bf16x8 (&qf
                                              float& m_run, float& l_run, f32x4 (&o)[8]) {
   const int g4 = lane >> 4, q = lane & 15;
   const float NEG_INF = -__builtin_huge_valf();
+  // keys past the sequence were loaded from its last row (finite), and their scores are
+  // replaced by -inf below, so the K operand needs no masking
   f32x4 s[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     s[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool kok = t0 + 16 * hf + q < T;
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-      const u32x4 kv = kok ? b.k[hf][dc] : u32x4{0u, 0u, 0u, 0u};
-      s[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[dc], s[hf], 0, 0, 0);
-    }
+    for (int dc = 0; dc < 4; ++dc)
+      s[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[hf][dc]), qf[dc], s[hf], 0, 0, 0);
   }
   // s[hf][r] = score of key t0 + 16*hf + 4*(L/16) + r for query L%16, kept in base-2
   // units (scaled by log2(e) / sqrt(128)) so every exponential is one hardware exp2;
@@ -186,14 +185,13 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (wave < nblk) {
+    // padding query rows (mq >= M) attend with row 0's query: finite, and their outputs
+    // are written as zero codes
     const int mq = mb * 16 + q;
     const uint16_t* qrow = p.q + (size_t)(mq < M ? mq : 0) * nq + h * HD + 8 * g4;
     bf16x8 qf[4];
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * dc);
-      qf[dc] = __builtin_bit_cast(bf16x8, mq < M ? v : u32x4{0u, 0u, 0u, 0u});
-    }
+    for (int dc = 0; dc < 4; ++dc) qf[dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * dc));
     KVBlock cur;
     load_block(cur, p, c0 + 32 * wave, lane);
     if constexpr (!MULTI) {
