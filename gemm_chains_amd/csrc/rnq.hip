@@ -34,12 +34,12 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
   const int K = p.K;
   __shared__ float wsum[4];
   const int rows = p.operand ? p.MB * 16 : p.M;
-  if (m >= rows) {  // extra workgroups: read the following GEMMs' weights ahead
+  if (__builtin_expect(m >= rows, 0)) {  // extra workgroups: read the following GEMMs' weights ahead
     const unsigned v = touch_weights(p.touch[0], m, rows, p.touch_wgs) ^ touch_weights(p.touch[1], m, rows, p.touch_wgs);
     if (v == 0x9e3779b9u && p.sink) *p.sink = v;  // practically never taken
     return;
   }
-  if (m >= p.M) {  // padding rows of the operand: zero codes (only launched with an operand)
+  if (__builtin_expect(m >= p.M, 0)) {  // padding rows of the operand: zero codes (only with an operand)
     if constexpr (ODT != 0) {
 #pragma unroll
       for (int i = 0; i < G; ++i) {
