@@ -15,7 +15,7 @@
 // [128][ldv] (key index contiguous) so that every MFMA operand is one contiguous load.  Scores are bf16 x bf16
 // MFMAs (exact products, fp32 sums); probabilities multiply V as three bf16 pieces
 // (hi + mid + lo carry all 24 bits of the fp32 value), so the output is fp32-accurate.
-#include "frt_internal.hpp"
+#include "gemm_kernel.hpp"
 
 #include <stdlib.h>
 
@@ -85,7 +85,7 @@ __device__ __forceinline__ void load_block(KVBlock& b, const AttnParams& p, int 
 // Online-softmax update of one wave's state with one 32-key block.
 __device__ __forceinline__ void attend_block(const KVBlock& b, const bf16x8 (&qf)[4], int t0, int lane, int T,
                                              float& m_run, float& l_run, f32x4 (&o)[8]) {
-  const int g4 = lane >> 4, q = lane & 15;
+  const int g4 = lane >> 4;
   const float NEG_INF = -__builtin_huge_valf();
   // keys past the sequence were loaded from its last row (finite), and their scores are
   // replaced by -inf below, so the K operand needs no masking
@@ -253,21 +253,21 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
   }
 }
 
-// Merge of the chunk records: workgroup = (head h, 16-row block mb); thread -> (query row,
-// 8 d); chunks in order (deterministic).  With CH > 0 (nch <= CH) every record of the
-// thread is loaded before the first is used, so the records, written by the previous
-// kernel on other XCDs, cost one memory latency instead of one per chunk.
-template <int CH, int ODT>
-__global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, int nch) {
-  const int h = blockIdx.x, mb = blockIdx.y, MB = gridDim.y;
-  const int tq = threadIdx.x >> 4;
-  const int d0 = (threadIdx.x & 15) * 8;
+// Merge of the chunk records of (head h, 16-row block mb) for one thread: query row tq,
+// d0 .. d0+7; chunks in order (deterministic).  With CH > 0 (nch <= CH) every record of
+// the thread is loaded before the first is used, so the records, written by the previous
+// kernel on other XCDs, cost one memory latency instead of one per chunk; slots past the
+// last chunk load chunk 0 again (always valid) and weigh it 0.  Maxima are in base-2
+// units (see attend_block).
+template <int CH>
+__device__ __forceinline__ void merge_records(const AttnParams& p, int h, int mb, int MB, int nch, int tq, int d0,
+                                              float (&o)[8]) {
   const float NEG_INF = -__builtin_huge_valf();
   const float* rec0 = p.workspace + ((size_t)h * MB + mb) * attn_record_floats();
   const size_t cstride = (size_t)p.n_heads * MB * attn_record_floats();
   float mx = NEG_INF, den = 0.f, num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto add = [&](float mc, float lc, f32x4 a, f32x4 b) {
-    const float wc = mc == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mc - mx);  // base-2 maxima
+    const float wc = mc == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mc - mx);
     den += wc * lc;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -276,8 +276,6 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
     }
   };
   if constexpr (CH > 0) {
-    // slots past the last chunk load chunk 0 again (always valid) and weigh it 0, so
-    // every load is unconditional and all are issued together
     float mc[CH], lc[CH];
     f32x4 a[CH], b[CH];
 #pragma unroll
@@ -288,6 +286,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
       a[c] = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0);
       b[c] = *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0 + 4);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every record load issued before the first wait
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (c >= nch) mc[c] = NEG_INF;
@@ -303,18 +302,99 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
           *reinterpret_cast<const f32x4*>(rc + 32 + tq * HD + d0 + 4));
     }
   }
+  const float rden = 1.0f / den;  // one division; the products are within an ulp of the quotients
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = num[e] * rden;
+}
+
+// Merge kernel: workgroup = (head h, 16-row block mb); thread -> (query row, 8 d).
+template <int CH, int ODT>
+__global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, int nch) {
+  const int h = blockIdx.x, mb = blockIdx.y, MB = gridDim.y;
+  const int tq = threadIdx.x >> 4;
+  const int d0 = (threadIdx.x & 15) * 8;
+  float o[8];
+  merge_records<CH>(p, h, mb, MB, nch, tq, d0, o);
   const float os = load_scale(p.out_scale_ptr, p.out_scale);
   const int m = mb * 16 + tq;
   const int k = h * HD + d0;
-  const float rden = 1.0f / den;  // one division; the products are within an ulp of the quotients
-  float o[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = num[e] * rden;
   store_operand4(p.operand, ODT, MB, m, k, o[0], o[1], o[2], o[3], os, m >= p.M);
   store_operand4(p.operand, ODT, MB, m, k + 4, o[4], o[5], o[6], o[7], os, m >= p.M);
   if (m < p.M) {
     record_amax(p.amax, o[0], o[1], o[2], o[3]);
     record_amax(p.amax, o[4], o[5], o[6], o[7]);
+  }
+}
+
+// The merge fused with the O projection (the chain, when the key axis is split):
+// workgroup = (head h, 16-row block mb, column group cg of 256 output columns).  Its 256
+// threads merge the records of (h, mb) exactly as attn_combine_kernel does and quantise
+// the 16 x 128 head output into that head's packed operand tiles in LDS; its 4 waves
+// then multiply them by the head's 128 rows of the O weight, 4 column tiles each, and
+// write split h of the O projection's partial sums (split-K over heads: split j is head
+// j).  Per column tile the k-steps of the head are separate MFMAs added in k-step order,
+// as the O GEMM with one split per head adds its waves' sums, so the partials are
+// bitwise those of the merge kernel followed by that GEMM.  The weight loads are issued
+// first and overlap the record loads.
+template <int DT, int CH>
+__global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams p, const GemmParams g, int nch) {
+  constexpr int ADT = act_dtype_of(DT);
+  constexpr int TBW = tile_bytes_of(DT), TBA = tile_bytes_of(ADT);
+  constexpr int KPH = HD / kstep_of(DT);  // k-steps per head: 4 (bf16) or 1 (e4m3, MXFP4)
+  constexpr int NTW = 4;                  // column tiles per wave
+  __shared__ __attribute__((aligned(16))) uint8_t opnd[KPH * TBA];
+  const int h = blockIdx.x, mb = blockIdx.y, cg = blockIdx.z, MB = gridDim.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pt0 = 16 * cg + NTW * wave;   // first column tile of this wave
+
+  Frag<DT> wf[NTW][KPH];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int kk = 0; kk < KPH; ++kk)
+      load_frag<DT, true>(wf[t][kk], g.w + ((size_t)(pt0 + t) * g.ksteps + h * KPH + kk) * TBW, lane);
+  __builtin_amdgcn_sched_barrier(0);  // the weight loads go out first
+
+  const int tq = threadIdx.x >> 4;
+  const int d0 = (threadIdx.x & 15) * 8;
+  float o[8];
+  merge_records<CH>(p, h, mb, MB, nch, tq, d0, o);
+  const float os = load_scale(p.out_scale_ptr, p.out_scale);
+  const int m = mb * 16 + tq;
+  store_operand4(opnd, ADT, 1, tq, d0, o[0], o[1], o[2], o[3], os, m >= p.M);
+  store_operand4(opnd, ADT, 1, tq, d0 + 4, o[4], o[5], o[6], o[7], os, m >= p.M);
+  if (m < p.M) {
+    record_amax(p.amax, o[0], o[1], o[2], o[3]);
+    record_amax(p.amax, o[4], o[5], o[6], o[7]);
+  }
+  __syncthreads();
+
+  Frag<ADT> af[KPH];
+#pragma unroll
+  for (int kk = 0; kk < KPH; ++kk) load_frag<ADT, false>(af[kk], opnd + kk * TBA, lane);
+  // The sums pass through LDS and a barrier before the (row-masked) stores: MFMAs ignore
+  // EXEC, and without this the compiler may sink them, and the per-lane scale operands
+  // they read, into the masked store block, where lanes of padding rows hold stale values.
+  __shared__ f32x4 res[4][NTW][64];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    f32x4 acc[KPH];
+#pragma unroll
+    for (int kk = 0; kk < KPH; ++kk) acc[kk] = mma(wf[t][kk], af[kk], f32x4{0.f, 0.f, 0.f, 0.f});
+    f32x4 v = acc[0];
+#pragma unroll
+    for (int kk = 1; kk < KPH; ++kk) v += acc[kk];
+    res[wave][t][lane] = v;
+  }
+  __syncthreads();
+  const int mrow = mb * 16 + (lane & 15);
+  if (mrow < g.M) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const int n0 = (pt0 + t) * 16 + 4 * (lane >> 4);
+      *reinterpret_cast<f32x4*>(g.partials + ((size_t)h * g.M + mrow) * g.N + n0) = res[wave][t][lane];
+    }
   }
 }
 
@@ -348,6 +428,35 @@ hipError_t launch_attention(const AttnParams& p_in, hipStream_t s) {
   else if (nch <= 16) launch_combine<16>(p, nch, s);
   else launch_combine<0>(p, nch, s);
   return hipGetLastError();
+}
+
+// Key chunks with partial records, then the merge fused with the O projection (`g` is the
+// O GEMM's parameters with one split per head; the caller checks attention_oproj_fusable).
+hipError_t launch_attention_oproj(const AttnParams& p_in, const GemmParams& g, hipStream_t s) {
+  AttnParams p = p_in;
+  p.chunk_keys = attention_chunk_keys(p.M, p.n_heads, p.kv_len);
+  const int nch = (p.kv_len + p.chunk_keys - 1) / p.chunk_keys;
+  const dim3 gc(p.n_heads, p.MB, nch);
+  if (p.chunk_keys <= 64) launch_chunk<2, false, true>(p, gc, s);
+  else launch_chunk<4, false, true>(p, gc, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 gm(p.n_heads, p.MB, g.N / 256), b(256);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, gm, b, 0, s, p, g, nch); };
+  const bool wide = nch > 8;
+  switch (g.ab_dtype) {
+    case FRT_BF16: wide ? go(attn_merge_oproj_kernel<FRT_BF16, 16>) : go(attn_merge_oproj_kernel<FRT_BF16, 8>); break;
+    case FRT_E4M3: wide ? go(attn_merge_oproj_kernel<FRT_E4M3, 16>) : go(attn_merge_oproj_kernel<FRT_E4M3, 8>); break;
+    default: wide ? go(attn_merge_oproj_kernel<FRT_MXFP4, 16>) : go(attn_merge_oproj_kernel<FRT_MXFP4, 8>); break;
+  }
+  return hipGetLastError();
+}
+
+// The fused pair applies when the key axis is cut into 2..16 chunks of at most 128 keys
+// and the O projection's width is a multiple of 256.
+bool attention_oproj_fusable(int M, int n_heads, int kv_len, int N) {
+  const int ck = attention_chunk_keys(M, n_heads, kv_len), nch = (kv_len + ck - 1) / ck;
+  return ck <= 128 && nch > 1 && nch <= 16 && N % 256 == 0;
 }
 
 int attention_kernel_count(int M, int n_heads, int kv_len) {

@@ -28,6 +28,7 @@ struct Buf {
 
 struct ChainLayout {
   int s_qkv = 0, s_o = 0, s_up = 0, s_down = 0;
+  bool fuse_o = false;                                     // attention merge fused with the O projection
   int nqkv = 0, nattn = 0;
   int kv_len = 0;                                          // prefix + own rows
   int ldv = 0;                                             // V^T row length (kv_len padded to 32)
@@ -82,6 +83,15 @@ static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
   L.nattn = d->n_heads * d->head_dim;
   L.s_qkv = resolve_split(d->splits_qkv, M, L.nqkv, H, dt, kEpiQkv);
   L.s_o = resolve_split(d->splits_o, M, H, L.nattn, dt, FRT_EPI_NONE);
+  // The attention merge runs inside the O projection when the key axis is split: that
+  // projection then has one split per head.  Debug runs keep the two apart (so the
+  // attention output can be inspected) with the same split, which makes them bitwise
+  // equal to the fused chain.
+  const int kv_len = d->prefix_len + M;
+  if ((d->splits_o == 0 || d->splits_o == d->n_heads) && attention_oproj_fusable(M, d->n_heads, kv_len, H)) {
+    L.s_o = d->n_heads;
+    L.fuse_o = !d->keep_intermediates;
+  }
   L.s_up = resolve_split(d->splits_up, M, 2 * F, H, dt, FRT_EPI_SILU_GATE_QUANT);
   L.s_down = resolve_split(d->splits_down, M, H, F, dt, FRT_EPI_NONE);
   const int ks = kstep_of(dt);
@@ -271,10 +281,16 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
       t.out_dtype = adt; t.out_scale = 1.f; t.out_scale_ptr = actp(l, SITE_O);
       t.operand = a_o; t.workspace = (float*)at(c, L.aws);
       t.amax = amax ? amax + l * 4 + SITE_O : nullptr;
-      FRT_HIP(launch_attention(t, s)); n += attention_kernel_count(M, d.n_heads, L.kv_len);
-
-      // 4. O projection -> partials
-      FRT_HIP(launch_gemm(go, s)); ++n;
+      if (L.fuse_o) {
+        // 3+4. key chunks, then their merge fused with the O projection -> partials
+        GemmParams gm = go;
+        gm.ksteps = L.nattn / kstep_of(d.dtype);
+        FRT_HIP(launch_attention_oproj(t, gm, s)); n += 2;
+      } else {
+        FRT_HIP(launch_attention(t, s)); n += attention_kernel_count(M, d.n_heads, L.kv_len);
+        // 4. O projection -> partials
+        FRT_HIP(launch_gemm(go, s)); ++n;
+      }
 
       // 5. producer: gated residual of the attention output, AdaRMSNorm (MLP sublayer)
       RnqParams b = a;
@@ -397,7 +413,8 @@ extern "C" int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_de
     c->kernels = n;
   } else {
     // count the launches without enqueueing anything
-    const int per_layer = 6 + attention_kernel_count(c->d.M, c->d.n_heads, c->L.kv_len) + (c->L.s_up > 1) + (c->L.s_qkv > 1);
+    const int attn_o = c->L.fuse_o ? 2 : attention_kernel_count(c->d.M, c->d.n_heads, c->L.kv_len) + 1;
+    const int per_layer = 5 + attn_o + (c->L.s_up > 1) + (c->L.s_qkv > 1);
     c->kernels = desc->steps * desc->layers * per_layer + 1;
   }
   *out = c;

@@ -384,6 +384,7 @@ constexpr int kEpiQkv = 4;   // reduce + scale recovery + bf16, scattered into Q
 
 size_t attention_workspace_bytes(int M, int n_heads, int kv_len);
 int attention_kernel_count(int M, int n_heads, int kv_len);
+bool attention_oproj_fusable(int M, int n_heads, int kv_len, int N);
 
 // Launchers (stream-ordered, no validation: callers validate first).
 hipError_t launch_rnq(const RnqParams& p, hipStream_t s);
@@ -391,6 +392,8 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 // What launch_gemm(p) will read of p.w, as touch units; split into `parts` parts.
 WeightTouch gemm_weight_touch(const GemmParams& p, int part, int parts);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+// attention key chunks, then their merge fused with the O projection (one split per head)
+hipError_t launch_attention_oproj(const AttnParams& p, const GemmParams& o_proj, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 // Library choices of split count and waves per workgroup.
 int choose_splits(int M, int N, int K, int dtype, int epi);

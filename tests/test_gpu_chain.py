@@ -123,7 +123,11 @@ def test_chain_parity(F, dtype, M, splits):
     chain.load_workload(ce, wl, scales)
     ce.run()
     torch.cuda.synchronize()
-    assert np.array_equal(ce.read("x_out").reshape(M, -1), got), "eager vs graph replay"
+    # without debug buffers the attention merge runs inside the O projection (one kernel
+    # fewer per layer when the library picks the splits); the sums are bitwise the same
+    assert np.array_equal(ce.read("x_out").reshape(M, -1), got), "eager, merge fused into the O projection, vs graph"
+    if splits == (0, 0, 0, 0):
+        assert ce.kernel_count() == cg.kernel_count() - dims["steps"] * dims["layers"]
     cg.close()
     ce.close()
 
