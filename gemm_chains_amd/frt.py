@@ -97,6 +97,10 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
                                "(run python -c 'import __graft_entry__ as g; g.build()')")
+        # torch ships its own HIP runtime under the same soname as the system one that the
+        # library links; whichever loads first serves the whole process, and torch needs
+        # its own, so torch is imported before the library is loaded
+        import torch  # noqa: F401
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(lib, name)

@@ -132,6 +132,34 @@ def test_chain_parity(F, dtype, M, splits):
     ce.close()
 
 
+@pytest.mark.parametrize("M", [50, 10])
+def test_full_decision_parity(F, M):
+    """The benchmark's workload in its launch configuration: 18 layers x 10 flow steps,
+    bf16, graph replay with the weight read-ahead, the attention merge fused into the O
+    projection.  End to end against the float64 oracle, bar from the oracle's own
+    sensitivity (2^-22 relative noise on every GEMM input, 8x)."""
+    frt, chain = F
+    dims = synth.chain_dims(layers=18, steps=10, M=M)
+    wl = synth.workload4(dims)
+    ws = _oracle_weights(wl["layers"], "bf16")
+    want = _oracle_run(wl, ws, None, "bf16")
+    g = np.random.default_rng(96)
+    sens = rel_l2(_oracle_run(wl, ws, None, "bf16",
+                              perturb=lambda v: v * (1.0 + 2.0 ** -22 * g.standard_normal(v.shape))), want)
+    bar = 8 * max(sens, 1e-7)
+    packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
+    ch = chain.Chain(dims, packed, use_graph=True, prefetch_next=True)
+    chain.load_workload(ch, wl)
+    ch.run()
+    torch.cuda.synchronize()
+    got = ch.read("x_out").reshape(M, -1)
+    err = rel_l2(got, want)
+    print(f"full decision M={M}: rel L2 {err:.3e}, oracle sensitivity {sens:.3e}, kernels {ch.kernel_count()}")
+    assert ch.kernel_count() == 7 * 18 * 10 + 1
+    assert err <= bar
+    ch.close()
+
+
 def test_weight_read_ahead_leaves_results_bit_identical(F):
     """Reading the down weights ahead (prefetch_next) only reads; outputs must not change."""
     frt, chain = F
