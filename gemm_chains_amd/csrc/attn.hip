@@ -327,26 +327,26 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
 }
 
 // The merge fused with the O projection (the chain, when the key axis is split):
-// workgroup = (head h, 16-row block mb, column group cg of 256 output columns).  Its 256
-// threads merge the records of (h, mb) exactly as attn_combine_kernel does and quantise
-// the 16 x 128 head output into that head's packed operand tiles in LDS; its 4 waves
-// then multiply them by the head's 128 rows of the O weight, 4 column tiles each, and
+// workgroup = (head h, 16-row block mb, column group cg of 64 * NTW output columns).  Its
+// 256 threads merge the records of (h, mb) exactly as attn_combine_kernel does and
+// quantise the 16 x 128 head output into that head's packed operand tiles in LDS; its 4
+// waves then multiply them by the head's 128 rows of the O weight, NTW column tiles each
+// (NTW chosen so that there are at least 128 workgroups), and
 // write split h of the O projection's partial sums (split-K over heads: split j is head
 // j).  Per column tile the k-steps of the head are separate MFMAs added in k-step order,
 // as the O GEMM with one split per head adds its waves' sums, so the partials are
 // bitwise those of the merge kernel followed by that GEMM.  The weight loads are issued
 // first and overlap the record loads.
-template <int DT, int CH>
+template <int DT, int CH, int NTW>
 __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams p, const GemmParams g, int nch) {
   constexpr int ADT = act_dtype_of(DT);
   constexpr int TBW = tile_bytes_of(DT), TBA = tile_bytes_of(ADT);
   constexpr int KPH = HD / kstep_of(DT);  // k-steps per head: 4 (bf16) or 1 (e4m3, MXFP4)
-  constexpr int NTW = 4;                  // column tiles per wave
   __shared__ __attribute__((aligned(16))) uint8_t opnd[KPH * TBA];
   const int h = blockIdx.x, mb = blockIdx.y, cg = blockIdx.z, MB = gridDim.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int pt0 = 16 * cg + NTW * wave;   // first column tile of this wave
+  const int pt0 = 4 * NTW * cg + NTW * wave;   // first column tile of this wave
 
   Frag<DT> wf[NTW][KPH];
 #pragma unroll
@@ -441,14 +441,21 @@ hipError_t launch_attention_oproj(const AttnParams& p_in, const GemmParams& g, h
   else launch_chunk<4, false, true>(p, gc, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 gm(p.n_heads, p.MB, g.N / 256), b(256);
+  // column tiles per wave: the widest that still gives at least 128 workgroups
+  const int base = p.n_heads * p.MB * (g.N / 256);
+  const int ntw = base >= 128 ? 4 : (2 * base >= 128 ? 2 : 1);
+  const dim3 gm(p.n_heads, p.MB, g.N / (64 * ntw)), b(256);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, gm, b, 0, s, p, g, nch); };
+  auto by_ntw = [&](auto k1, auto k2, auto k4) { ntw == 4 ? go(k4) : (ntw == 2 ? go(k2) : go(k1)); };
+#define FRT_MERGE_OPROJ(DT, CH) \
+  by_ntw(attn_merge_oproj_kernel<DT, CH, 1>, attn_merge_oproj_kernel<DT, CH, 2>, attn_merge_oproj_kernel<DT, CH, 4>)
   const bool wide = nch > 8;
   switch (g.ab_dtype) {
-    case FRT_BF16: wide ? go(attn_merge_oproj_kernel<FRT_BF16, 16>) : go(attn_merge_oproj_kernel<FRT_BF16, 8>); break;
-    case FRT_E4M3: wide ? go(attn_merge_oproj_kernel<FRT_E4M3, 16>) : go(attn_merge_oproj_kernel<FRT_E4M3, 8>); break;
-    default: wide ? go(attn_merge_oproj_kernel<FRT_MXFP4, 16>) : go(attn_merge_oproj_kernel<FRT_MXFP4, 8>); break;
+    case FRT_BF16: if (wide) FRT_MERGE_OPROJ(FRT_BF16, 16); else FRT_MERGE_OPROJ(FRT_BF16, 8); break;
+    case FRT_E4M3: if (wide) FRT_MERGE_OPROJ(FRT_E4M3, 16); else FRT_MERGE_OPROJ(FRT_E4M3, 8); break;
+    default: if (wide) FRT_MERGE_OPROJ(FRT_MXFP4, 16); else FRT_MERGE_OPROJ(FRT_MXFP4, 8); break;
   }
+#undef FRT_MERGE_OPROJ
   return hipGetLastError();
 }
 
