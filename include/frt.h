@@ -241,7 +241,14 @@ int frt_attention_prefix(void* stream, int M, int n_heads, int head_dim, int kv_
  * last layer of the last step a final producer adds the last MLP output into "x".
  * mod rows are (scale, shift, gate); the producer that starts layer l uses layer l's
  * modulation while reducing layer l-1's output (next-layer conditioning prepares the
- * next input: notes, static-quantisation section).                                   */
+ * next input: notes, static-quantisation section).
+ * When the key axis is cut into chunks (prefix_len + M > 128 keys at most 16 chunks) and
+ * hidden % 256 == 0, the attention merge runs inside the O projection: one kernel
+ * merges a head's chunk partials and multiplies the head output by that head's rows of
+ * W_o, so the O projection is split by head (splits_o resolves to n_heads; an explicit
+ * other value keeps the two apart).  Without debug buffers this saves one kernel per
+ * layer; with them the two run apart with the same split, and the results are bitwise
+ * the same.                                                                           */
 typedef struct frt_chain_desc {
   int layers, steps, M, hidden, n_heads, head_dim, prefix_len, mlp;
   int dtype;                 /* FRT_BF16 or FRT_E4M3 (weights and GEMM inputs), or
