@@ -257,11 +257,11 @@ typedef struct frt_chain_desc {
   int splits_qkv, splits_o, splits_up, splits_down;   /* 0 = library choice            */
   int use_graph;             /* 1: capture once, replay with one hipGraphLaunch          */
   int keep_intermediates;    /* 1: every (step, layer) writes its own debug buffers      */
-  int prefetch_next;         /* 1: the producer before the gate|up GEMM also reads the
-                                down projection's weights ahead, from extra workgroups on
-                                the XCDs that will stream them, so the down GEMM finds them
-                                in L2 (the launch-overlap analogue).  Results are bitwise
-                                unchanged.                                               */
+  int prefetch_next;         /* 1: each producer also reads the weights of a GEMM that
+                                follows it ahead (the first the QKV weights, the second
+                                the down projection's), from extra workgroups on the XCDs
+                                that will stream them, so the GEMM finds them in L2 (the
+                                launch-overlap analogue).  Results are bitwise unchanged. */
   /* host arrays of `layers` device pointers to packed weights (frt_pack_weight):
    * qkv [hidden][(n_heads+2)*head_dim] plain, o [n_heads*head_dim][hidden] plain,
    * up [hidden][2*mlp] FRT_W_GATE_UP, down [mlp][hidden] plain.                        */
