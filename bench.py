@@ -104,6 +104,50 @@ def time_dominant_gemm(torch, frt, device, synth, dims, dtype, reps=128):
     return time_gemm(torch, frt, device, synth, dims["M"], dims["hidden"], 2 * dims["mlp"], dtype, reps)
 
 
+class _Unrolled:
+    """The packed weights of the first `layers` layers of a stack, cloned `steps` times
+    (distinct addresses): layer k*layers + l of the unrolled chain is layer l at step k."""
+
+    def __init__(self, packed, steps, layers=None):
+        self.dtype = packed.dtype
+        self.w = {k: [t.clone() for _ in range(steps) for t in v[:layers]] for k, v in packed.w.items()}
+        self.s = {k: [None if t is None else t.clone() for _ in range(steps) for t in v[:layers]]
+                  for k, v in packed.s.items()}
+
+
+def cold_and_one_layer(torch, chain, synth, dims, packed, wl, steps, warmup, deployed_out):
+    """The decision with cold weights, and a one-layer graph for cross-checking.
+
+    Cold: the 18 x 10 decision unrolled into 180 layers x 1 step whose weights are 180
+    distinct copies (5.4 GB bf16), so no weight is read twice per decision; the math is
+    the same, so x_out must equal the deployed chain's bit for bit.  One layer: a graph of
+    a single layer (its 7 kernels plus the final producer), replayed alone.
+    """
+    S, L = dims["steps"], dims["layers"]
+    dims_c = dict(dims, layers=S * L, steps=1)
+    wl_c = dict(x0=wl["x0"], mod=wl["mod"].reshape((1, S * L) + wl["mod"].shape[2:]), dims=dims_c,
+                layers=[wl["layers"][i % L] for i in range(S * L)])
+    un = _Unrolled(packed, S)
+    ch = chain.Chain(dims_c, un, use_graph=True, prefetch_next=True)
+    chain.load_workload(ch, wl_c)
+    torch.cuda.synchronize()
+    ms = time_chain(torch, ch, steps, warmup)
+    same = bool((ch.read("x_out") == deployed_out).all())
+    ch.close()
+    del un
+    torch.cuda.empty_cache()
+    dims_1 = dict(dims, layers=1, steps=1)
+    wl_1 = dict(x0=wl["x0"], mod=wl["mod"][:1, :1], dims=dims_1, layers=wl["layers"][:1])
+    p1 = _Unrolled(packed, 1, layers=1)
+    c1 = chain.Chain(dims_1, p1, use_graph=True, prefetch_next=True)
+    chain.load_workload(c1, wl_1)
+    torch.cuda.synchronize()
+    ms1 = time_chain(torch, c1, 200, 20)
+    c1.close()
+    return dict(cold_us_per_layer=round(ms * 1e3 / (S * L), 3), cold_matches_deployed_bitwise=same,
+                one_layer_graph_us=round(ms1 * 1e3, 3))
+
+
 def state_reuse(torch, chain, synth, dims, packed, wl, reps=20):
     """Execution-state capsule and selective refresh on the M=50 bf16 chain.
 
@@ -297,7 +341,12 @@ def main():
                 weight_gbs=(wb + kv_bytes(dims)) * dims["steps"] / (ms * 1e-3) / 1e9)
             log(f"M={M} {dt_name} prefetch={int(pf)}: {ch.kernel_count()} kernels, {ms:.3f} ms/decision, "
                 f"{ms * 1e3 / nl:.2f} us/layer")
+            if M == 50 and pf:
+                deployed_out = ch.read("x_out")
             ch.close()
+        if M == 50:
+            cold = cold_and_one_layer(torch, chain, synth, dims, packed, wl, args.steps, args.warmup, deployed_out)
+            log(f"cold weights / one layer: {cold}")
         # e4m3 chain: static activation scales from one bf16 run on the calibration inputs
         x0c, modc = synth.chain_inputs(dims, synth.CAL_SEED)
         cal = chain.Chain(dims, packed, use_graph=False)
@@ -391,6 +440,7 @@ def main():
                                     / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), 5),
         "gemm_sweep_k2048_n16384": sweep,
         "state_reuse_m50_bf16": reuse,
+        "cold_weights_m50_bf16": cold,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
