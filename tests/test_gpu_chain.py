@@ -132,6 +132,35 @@ def test_chain_parity(F, dtype, M, splits):
     ce.close()
 
 
+@pytest.mark.parametrize("M,prefix", [(1, 0), (64, 100), (17, 300), (50, 0)])
+def test_chain_edge_shapes(F, M, prefix):
+    """Smallest and largest action chunks and short prefixes: no prefix (one key chunk,
+    the merge kernel not needed), and prefixes that give 2..4 chunks (merge fused into
+    the O projection).  bf16, against the oracle chain; the production chain (fused,
+    read-ahead on) must equal the unfused debug chain bit for bit."""
+    frt, chain = F
+    dims = synth.chain_dims(layers=2, steps=2, M=M, prefix=prefix)
+    wl = synth.workload4(dims)
+    ws = _oracle_weights(wl["layers"], "bf16")
+    want = _oracle_run(wl, ws, None, "bf16")
+    g = np.random.default_rng(97)
+    sens = rel_l2(_oracle_run(wl, ws, None, "bf16",
+                              perturb=lambda v: v * (1.0 + 2.0 ** -22 * g.standard_normal(v.shape))), want)
+    packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
+    outs = []
+    for dbg, pf in ((True, False), (False, True)):
+        ch = chain.Chain(dims, packed, use_graph=True, keep_intermediates=dbg, prefetch_next=pf)
+        chain.load_workload(ch, wl)
+        ch.run()
+        torch.cuda.synchronize()
+        outs.append(ch.read("x_out").reshape(M, -1))
+        ch.close()
+    err = rel_l2(outs[1], want)
+    print(f"chain M={M} prefix={prefix}: rel L2 {err:.3e}, oracle sensitivity {sens:.3e}")
+    assert err <= 8 * max(sens, 1e-6)
+    assert np.array_equal(outs[0], outs[1]), "production (fused, read-ahead) vs debug chain"
+
+
 @pytest.mark.parametrize("M", [50, 10])
 def test_full_decision_parity(F, M):
     """The benchmark's workload in its launch configuration: 18 layers x 10 flow steps,
