@@ -264,7 +264,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
       a.amax = amax ? amax + l * 4 + SITE_QKV : nullptr;
       a.sink = sink;
       if (pf) {  // read the QKV GEMM's weights ahead
-        a.touch[0] = gemm_weight_touch(gq, 0, 1);
+        a.touch = gemm_weight_touch(gq, 0, 1);
         a.touch_wgs = touch_wgs;
       }
       FRT_HIP(launch_rnq(a, s)); ++n;
@@ -306,7 +306,7 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
       b.act_scale_ptr = actp(l, SITE_UP); b.operand = a_up;
       b.amax = amax ? amax + l * 4 + SITE_UP : nullptr;
       if (pf) {
-        b.touch[0] = gemm_weight_touch(gd, 0, 1);
+        b.touch = gemm_weight_touch(gd, 0, 1);
         b.touch_wgs = touch_wgs;
       }
       FRT_HIP(launch_rnq(b, s)); ++n;

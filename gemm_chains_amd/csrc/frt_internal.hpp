@@ -313,7 +313,7 @@ struct RnqParams {
   const float* act_scale_ptr;
   uint8_t* operand;          // packed or null
   unsigned* amax;            // calibration: running max |value before rounding| (float bits), or null
-  WeightTouch touch[2];      // weights of following GEMMs read ahead by extra workgroups
+  WeightTouch touch;         // weights of a following GEMM read ahead by extra workgroups
   int touch_wgs;             // extra workgroups after the rows (a multiple of 8), or 0
   unsigned* sink;            // never written in practice (keeps the touch loads)
 };
