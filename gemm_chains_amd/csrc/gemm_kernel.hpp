@@ -213,8 +213,10 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
   // SiLU-gate epilogue: packed tiles 2i (gate) and 2i+1 (up) of this workgroup pair up;
   // padding rows of the output operand get zero codes
   auto finish_pair = [&](int tp, int b, f32x4 vg, f32x4 vu) {
-    const int ng = logical_tile_of(p.layout, p.N, g * NT + 2 * tp) * 16 + 4 * (lane >> 4);
-    const int nu = logical_tile_of(p.layout, p.N, g * NT + 2 * tp + 1) * 16 + 4 * (lane >> 4);
+    // the in-kernel SiLU epilogue runs only on FRT_W_GATE_UP weights: packed tiles 2i and
+    // 2i+1 are gate tile i and up tile i
+    const int ng = ((g * NT) / 2 + tp) * 16 + 4 * (lane >> 4);
+    const int nu = ng + p.N / 2;
     const int m = (mb0 + b) * 16 + (lane & 15);
     f32x4 cg = vg * as, cu = vu * as;
     if (!PLAIN && p.colscale) {
