@@ -189,6 +189,36 @@ def test_full_decision_parity(F, M):
     ch.close()
 
 
+@pytest.mark.parametrize("dtype", ["e4m3", "mxfp4"])
+def test_full_decision_fp8_and_4bit_properties(F, dtype):
+    """The 18 x 10 decision at M=50 with e4m3 activations (e4m3 or MXFP4 weights), scales
+    calibrated on the GPU: the production chain (graph, read-ahead, merge fused into the
+    O projection) equals the unfused debug chain bit for bit, and every output is finite.
+    (End-to-end parity against the oracle at this size is the bf16 test above; the fp8 and
+    4-bit paths are held to the oracle at 2 layers x 2 steps.)"""
+    frt, chain = F
+    dims = synth.chain_dims(layers=18, steps=10, M=50)
+    wl = synth.workload4(dims)
+    pb = chain.PackedLayers(wl["layers"], dims, frt.BF16)
+    x0c, modc = synth.chain_inputs(dims, synth.CAL_SEED)
+    cal = chain.Chain(dims, pb, use_graph=False)
+    chain.load_workload(cal, dict(wl, x0=x0c, mod=modc))
+    scales = cal.calibrate().cpu().numpy()
+    cal.close()
+    del pb
+    packed = chain.PackedLayers(wl["layers"], dims, frt.DTYPES[dtype])
+    outs = []
+    for dbg, pf in ((True, False), (False, True)):
+        ch = chain.Chain(dims, packed, use_graph=True, keep_intermediates=dbg, prefetch_next=pf)
+        chain.load_workload(ch, wl, scales)
+        ch.run()
+        torch.cuda.synchronize()
+        outs.append(ch.read("x_out"))
+        ch.close()
+    assert np.isfinite(outs[1]).all()
+    assert np.array_equal(outs[0], outs[1]), "production vs debug chain"
+
+
 def test_weight_read_ahead_leaves_results_bit_identical(F):
     """Reading the down weights ahead (prefetch_next) only reads; outputs must not change."""
     frt, chain = F
