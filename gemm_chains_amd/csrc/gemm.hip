@@ -86,9 +86,16 @@ static int per_max(int dtype, int nt, int mbw) {
   return per;
 }
 
-// Measured on MI355X at the action-decoder shapes (M = 10/50, K = 1024..4096):
-//  - widest column group (NT = 4, 2, 1) that still leaves >= 256 workgroups; the SiLU
-//    epilogue needs gate/up pairs (even NT);
+// Measured on MI355X at the action-decoder shapes (M = 10/50, K = 1024..4096) and the
+// K = 2048, N = 16384 gate|up sweep:
+//  - widest column group (NT = 4, 2, 1) that still leaves >= 512 workgroups, i.e. two
+//    per CU: a read-rate probe of the GEMM's own weight pattern streams 64 MB at 5.7 TB/s
+//    with 512 workgroups of 2 tiles against 4.6 TB/s with 256 of 4 (the same bytes in
+//    flight per CU, twice the waves); the sweep's bf16 GEMM at M <= 16 went from 15.9 to
+//    12.8 us, e4m3 from 8.1-11.0 to 7.7-10.0 us, and every chain by 0.1-0.5 us/layer (the
+//    down projection).  MXFP4 weights with the SiLU epilogue keep >= 256 (5.25 against
+//    5.5 us at M = 1): their 1088-byte tiles are small next to the activation tiles every
+//    extra workgroup re-reads.  The SiLU epilogue needs gate/up pairs (even NT);
 //  - when even the narrowest group leaves fewer than 256 workgroups, the row blocks are
 //    spread over row groups (one block each) on the column group's XCD;
 //  - four waves per workgroup, each with as many k-steps per round as its registers
@@ -102,9 +109,10 @@ static GemmShape choose_shape(const GemmParams& p) {
   else sh.epi = p.epi == kEpiQkv ? kGemmQkv : kGemmStore;
   const int nt_min = sh.epi == kGemmSiluBf16 || sh.epi == kGemmSiluE4m3 ? 2 : 1;
   sh.nt = nt_min;
+  const int wg_target = p.ab_dtype == FRT_MXFP4 && nt_min == 2 ? 256 : 512;
   for (int cand : {4, 2}) {
     if (tiles % cand || cand < nt_min) continue;
-    if ((tiles / cand) * p.splits >= 256) { sh.nt = cand; break; }
+    if ((tiles / cand) * p.splits >= wg_target) { sh.nt = cand; break; }
   }
   if (tiles % sh.nt) sh.nt = 1;
   sh.col_groups = tiles / sh.nt;

@@ -111,10 +111,11 @@ __device__ __forceinline__ float silu_f(float g) {
 }
 
 // Workgroup = (column-tile group g, row group r, K-chunk `split`).  Its kw waves split the
-// chunk's k-steps into contiguous runs of PER * rounds; in each round a wave issues all
-// of its PER k-steps' weight and activation loads before its first wait (a scheduling
-// barrier keeps the compiler from interleaving them with the MFMAs, which would put a
-// memory round trip between every few MFMAs), then runs the MFMAs.  The waves' sums are
+// chunk's k-steps into contiguous runs of PER * rounds; a wave issues its first PER
+// k-steps' weight and activation loads before its first wait (a scheduling barrier keeps
+// the compiler from interleaving them with the MFMAs, which would put a memory round trip
+// between every few MFMAs), then, with more rounds, reloads each k-step slot with the next
+// round's k-step right after that slot's MFMAs (a rolling pipeline).  The waves' sums are
 // added in LDS in wave order, so results are bitwise deterministic and independent of
 // the row grouping.  Row groups (XCD-aware: the groups that share a column group are
 // eight workgroup ids apart, so they run on one XCD and its L2 serves the weight tile
@@ -164,26 +165,41 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int b = 0; b < MB; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int ks0 = ks_begin;
-  do {  // run = PER * rounds, rounds >= 1
-    Frag<DT> wf[PER][NT];
-    Frag<ADT> af[PER][MB];
+  // PER k-step slots of weight and activation fragments; slot u first holds k-step
+  // ks_begin + u.  run = PER * rounds, rounds >= 1.
+  Frag<DT> wf[PER][NT];
+  Frag<ADT> af[PER][MB];
+  auto load_slot = [&](int u, int ks) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
+    for (int t = 0; t < NT; ++t) load_frag<DT, true>(wf[u][t], wbase[t] + (size_t)ks * TBW, lane);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) load_frag<DT, true>(wf[u][t], wbase[t] + (size_t)(ks0 + u) * TBW, lane);
+    for (int b = 0; b < MB; ++b) load_frag<ADT, false>(af[u][b], abase + (size_t)ks * astep + (size_t)b * TB, lane);
+  };
+  auto mma_slot = [&](int u) {
 #pragma unroll
-      for (int b = 0; b < MB; ++b) load_frag<ADT, false>(af[u][b], abase + (size_t)(ks0 + u) * astep + (size_t)b * TB, lane);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int b = 0; b < MB; ++b) acc[t][b] = mma(wf[u][t], af[u][b], acc[t][b]);
+  };
+#pragma unroll
+  for (int u = 0; u < PER; ++u) load_slot(u, ks_begin + u);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!SHAPE) {
+    // Rolling pipeline over the further rounds: as soon as slot u's MFMAs have read it,
+    // the slot is reloaded with the same slot of the next round, so a full round of loads
+    // stays in flight instead of each round waiting for the last one's data and sums.
+    const int rounds = run / PER;
+    for (int r = 1; r < rounds; ++r) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        mma_slot(u);
+        load_slot(u, ks_begin + r * PER + u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) acc[t][b] = mma(wf[u][t], af[u][b], acc[t][b]);
-    ks0 += PER;
-  } while (!SHAPE && ks0 < ks_begin + run);
+  for (int u = 0; u < PER; ++u) mma_slot(u);  // the last (or only) round
   if (!active) return;  // whole workgroup
 
   // ---- epilogue (one per kernel)
