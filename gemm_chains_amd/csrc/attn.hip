@@ -109,8 +109,8 @@ __device__ __forceinline__ void attend_block(const KVBlock& b, const bf16x8 (&qf
       s[hf][r] = t0 + 16 * hf + 4 * g4 + r < T ? s[hf][r] * scale : NEG_INF;
       bmax = fmaxf(bmax, s[hf][r]);
     }
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+  bmax = xor_max<16>(bmax);
+  bmax = xor_max<32>(bmax);
   const float m_new = fmaxf(m_run, bmax);  // finite: the block holds a key < T
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   float pr[8];
@@ -208,8 +208,8 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
         }
       }
     }
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
+    l_run = xor_add<16>(l_run);
+    l_run = xor_add<32>(l_run);
   }
 
   // ---- merge the waves (wave order)

@@ -239,6 +239,49 @@ __device__ __forceinline__ void store_qkv4(uint16_t* q_out, uint16_t* k_out, uin
   }
 }
 
+// ------------------------------------------------------------------ cross-lane butterflies
+// One step of an xor butterfly over a 64-lane wave: v combined with the value of lane
+// (lane ^ OFF), on the VALU instead of the LDS permute path of __shfl_xor.  OFF = 16 and
+// 32 use the gfx950 lane swaps, which return the value pair (own, partner) in a
+// row-dependent order; OFF = 1, 2, 8 are one DPP move (quad permutes, a row rotation by
+// 8) and OFF = 4 is two (the half-row mirror, then a quad reversal).  Addition and
+// maximum are commutative, so every lane gets bitwise what v + __shfl_xor(v, OFF) (or
+// fmaxf) gives it.  All 64 lanes must be active.
+template <int OFF>
+__device__ __forceinline__ float xor_partner_dpp(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (OFF == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  else if constexpr (OFF == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  else if constexpr (OFF == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
+  else {
+    static_assert(OFF == 4, "DPP partner for OFF in {1, 2, 4, 8}");
+    const int m = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // lane 7 - i within 8
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false));  // then 3 - j within 4
+  }
+}
+template <int OFF>
+__device__ __forceinline__ float xor_add(float v) {
+  if constexpr (OFF == 16 || OFF == 32) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = OFF == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    return v + xor_partner_dpp<OFF>(v);
+  }
+}
+template <int OFF>
+__device__ __forceinline__ float xor_max(float v) {
+  if constexpr (OFF == 16 || OFF == 32) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = OFF == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    return fmaxf(v, xor_partner_dpp<OFF>(v));
+  }
+}
+
 // ------------------------------------------------------------------ weight touching
 // The packed weight bytes a following GEMM launch will read, described by that launch's
 // shape, so that a latency-bound kernel can read them ahead from workgroups on the same

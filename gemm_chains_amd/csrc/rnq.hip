@@ -122,8 +122,13 @@ __global__ void __launch_bounds__(256) rnq_kernel(const RnqParams p) {
     }
   }
   if constexpr (ODT != 0) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    // xor butterfly 32, 16, 8, 4, 2, 1 on the VALU (bitwise the __shfl_xor butterfly)
+    ss = xor_add<32>(ss);
+    ss = xor_add<16>(ss);
+    ss = xor_add<8>(ss);
+    ss = xor_add<4>(ss);
+    ss = xor_add<2>(ss);
+    ss = xor_add<1>(ss);
     if (lane == 0) wsum[wave] = ss;
     __syncthreads();
     const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
