@@ -243,25 +243,32 @@ __global__ void __launch_bounds__(64 * NW) attn_chunk_kernel(const AttnParams p)
       const f32x4 ov = acc * (1.0f / den);
       store_operand4(p.operand, ODT, MB, m, h * HD + d, ov.x, ov.y, ov.z, ov.w, os, m >= M);
       if (m < M) record_amax(p.amax, ov.x, ov.y, ov.z, ov.w);
-    } else {
+    } else if (m < M) {  // padding rows' records are never read
       *reinterpret_cast<f32x4*>(rec + 32 + tq * HD + d) = acc;
     }
   }
-  if (REC && (threadIdx.x % (128 / DPT)) == 0) {
+  if (REC && m < M && (threadIdx.x % (128 / DPT)) == 0) {
     rec[tq] = mx;
     rec[16 + tq] = den;
   }
 }
 
 // Merge of the chunk records of (head h, 16-row block mb) for one thread: query row tq,
-// d0 .. d0+7; chunks in order (deterministic).  With CH > 0 (nch <= CH) every record of
+// d0 .. d0+7; chunks in order (deterministic).  A padding row (live = false) has no
+// records (the chunk kernel writes none) and merges to zeros, which are written as zero
+// codes.  With CH > 0 (nch <= CH) every record of
 // the thread is loaded before the first is used, so the records, written by the previous
 // kernel on other XCDs, cost one memory latency instead of one per chunk; slots past the
 // last chunk load chunk 0 again (always valid) and weigh it 0.  Maxima are in base-2
 // units (see attend_block).
 template <int CH>
 __device__ __forceinline__ void merge_records(const AttnParams& p, int h, int mb, int MB, int nch, int tq, int d0,
-                                              float (&o)[8]) {
+                                              bool live, float (&o)[8]) {
+  if (!live) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    return;
+  }
   const float NEG_INF = -__builtin_huge_valf();
   const float* rec0 = p.workspace + ((size_t)h * MB + mb) * attn_record_floats();
   const size_t cstride = (size_t)p.n_heads * MB * attn_record_floats();
@@ -314,7 +321,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
   const int tq = threadIdx.x >> 4;
   const int d0 = (threadIdx.x & 15) * 8;
   float o[8];
-  merge_records<CH>(p, h, mb, MB, nch, tq, d0, o);
+  merge_records<CH>(p, h, mb, MB, nch, tq, d0, mb * 16 + tq < p.M, o);
   const float os = load_scale(p.out_scale_ptr, p.out_scale);
   const int m = mb * 16 + tq;
   const int k = h * HD + d0;
@@ -359,7 +366,7 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
   const int tq = threadIdx.x >> 4;
   const int d0 = (threadIdx.x & 15) * 8;
   float o[8];
-  merge_records<CH>(p, h, mb, MB, nch, tq, d0, o);
+  merge_records<CH>(p, h, mb, MB, nch, tq, d0, mb * 16 + tq < p.M, o);
   const float os = load_scale(p.out_scale_ptr, p.out_scale);
   const int m = mb * 16 + tq;
   store_operand4(opnd, ADT, 1, tq, d0, o[0], o[1], o[2], o[3], os, m >= p.M);
