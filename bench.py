@@ -293,6 +293,9 @@ def main():
     ap.add_argument("--dominant-only", action="store_true",
                     help="run only the dominant GEMM's timed graph and a plain copy of known size "
                          "(the program the HBM-traffic counter passes profile)")
+    ap.add_argument("--chain-only", action="store_true",
+                    help="run only the M=50 bf16 chain (read-ahead on) for --warmup + --steps decisions "
+                         "(the program the launch-gap kernel trace profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the single-batch action-decoder chain is a "
@@ -305,6 +308,20 @@ def main():
     from gemm_chains_amd import chain, device, frt
     frt.lib()
     torch.cuda.set_device(0)
+
+    if args.chain_only:
+        dims = synth.chain_dims(layers=args.layers, steps=args.flow_steps, M=50)
+        wl = synth.workload4(dims)
+        packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
+        ch = chain.Chain(dims, packed, use_graph=True, prefetch_next=True)
+        chain.load_workload(ch, wl)
+        torch.cuda.synchronize()
+        ms = time_chain(torch, ch, args.steps, args.warmup)
+        print(json.dumps({"chain_us_per_layer_m50_bf16": round(ms * 1e3 / (dims["layers"] * dims["steps"]), 3),
+                          "decisions": args.warmup + args.steps, "kernels_per_decision": ch.kernel_count()}),
+              flush=True)
+        ch.close()
+        return
 
     if args.dominant_only:
         dims = synth.chain_dims(layers=1, steps=1, M=50)
