@@ -233,20 +233,31 @@ GEMM_SOURCES = [os.path.join(ROOT, "gemm_chains_amd", "csrc", f)
                 for f in ("gemm.hip", "gemm_kernel.hpp", "gemm_bf16_silu.hip", "frt_internal.hpp")]
 
 
+def gemm_source_hash():
+    """Hash of the dominant kernel's sources with comments and blank lines removed, so a
+    change of wording does not void the counters, while any change of code does."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+        h.update(code.encode("utf-8"))
+    return h.hexdigest()[:16]
+
+
 def measured_traffic():
     """HBM bytes per launch of the dominant kernel from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a streaming kernel of known size), or None when the
-    kernel's sources changed since the counters were taken (hash recorded in the summary)."""
-    import hashlib
+    kernel's code changed since the counters were taken (hash recorded in the summary)."""
     try:
         text = open(TRAFFIC_PROFILE, encoding="utf-8").read()
     except OSError:
         return None
     fields = dict(l.split(":", 1) for l in text.splitlines() if l.startswith(("source_sha256:", "traffic_bytes_")))
-    h = hashlib.sha256()
-    for f in GEMM_SOURCES:
-        h.update(open(f, "rb").read())
-    if fields.get("source_sha256", "").strip() != h.hexdigest()[:16]:
+    if fields.get("source_sha256", "").strip() != gemm_source_hash():
         return None
     return int(fields["traffic_bytes_per_launch"].strip())
 

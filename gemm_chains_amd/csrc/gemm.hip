@@ -202,12 +202,11 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
 // Split-K choice (measured on MI355X at the action-decoder shapes).  When the GEMM ends
 // in an epilogue, s > 1 costs a separate consumer kernel (~1.6 us of graph dispatch plus
 // its own memory round trip), more than the extra parallelism buys: s = 1.  When the
-// partials are the output (the next producer reduces them anyway), split until there are
-// two workgroups per CU (512) while every chunk keeps at least 4 k-steps.
-// Partials as the output: split until one column tile per workgroup gives 256
-// workgroups, keeping >= 4 k-steps per chunk.  Every split adds an M x N fp32 slice that
-// the consumer reads back; in the chain's down projection (K = 4096, N = 1024, M = 50/10,
-// bf16 and e4m3) 4 splits beat 8 by 0.2-0.7 us per layer and 16 lost 1.2-2.6 us.
+// partials are the output (the next producer reduces them anyway), split until one
+// column tile per workgroup gives 256 workgroups, keeping >= 4 k-steps per chunk.  Every
+// split adds an M x N fp32 slice that the consumer reads back; in the chain's down
+// projection (K = 4096, N = 1024, M = 50/10, bf16 and e4m3) 4 splits beat 8 by
+// 0.2-0.7 us per layer and 16 lost 1.2-2.6 us.
 int choose_splits(int M, int N, int K, int dtype, int epi) {
   (void)M;
   if (epi != FRT_EPI_NONE) return 1;
