@@ -197,7 +197,10 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
   const bool pf = d.prefetch_next != 0;
   unsigned* sink = (unsigned*)at(c, L.sink);
   const int rows = MB * 16;
-  const int touch_wgs = ((256 - rows) / 8) * 8;  // fill the remaining CUs
+  // read-ahead workgroups: on the CUs the rows leave free, at most 160 (paired on
+  // MI355X: 128-160 beat the 192 / 240 that fill the free CUs by 0.03-0.15 us per layer
+  // at M = 50 / 10; 64 or 96 lose 0.4-1.3 us, each toucher then reads too much)
+  const int touch_wgs = ((256 - rows) / 8) * 8 < 160 ? ((256 - rows) / 8) * 8 : 160;
 
   const float* h_prev = (const float*)at(c, L.x_in);
   const float* pdown_prev = nullptr;
