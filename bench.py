@@ -53,6 +53,20 @@ def time_chain(torch, ch, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per decision
 
 
+def decision_spread(torch, ch, n):
+    """Per-decision times (ms) of n further replays, each bracketed by its own HIP events
+    on the replay stream: the spread behind the mean the timed region reports."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        ch.run(stream.cuda_stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return {q: t[min(n - 1, int(round(f * (n - 1))))] for q, f in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
+
+
 def time_gemm(torch, frt, device, synth, M, K, N, dtype, reps=128, pool_bytes=1 << 30):
     """One gate|up GEMM (M x K x N, SiLU-gate epilogue, the library's split) timed alone.
 
@@ -369,6 +383,9 @@ def main():
                 weight_gbs=(wb + kv_bytes(dims)) * dims["steps"] / (ms * 1e-3) / 1e9)
             log(f"M={M} {dt_name} prefetch={int(pf)}: {ch.kernel_count()} kernels, {ms:.3f} ms/decision, "
                 f"{ms * 1e3 / nl:.2f} us/layer")
+            if pf:
+                spread = decision_spread(torch, ch, max(10, args.steps))
+                results[(M, dt_name, pf)]["spread_us_layer"] = {q: round(v * 1e3 / nl, 3) for q, v in spread.items()}
             if M == 50 and pf:
                 deployed_out = ch.read("x_out")
             ch.close()
@@ -458,6 +475,8 @@ def main():
                   and results[(10, "mxfp4", False)]["finite"]},
         "us_per_layer_m10": round(results[10]["us_layer"], 3),
         "ms_per_decision_m10": round(results[10]["ms"], 4),
+        "per_decision_us_per_layer_read_ahead_on": {"m50": results[(50, "bf16", True)]["spread_us_layer"],
+                                                    "m10": results[(10, "bf16", True)]["spread_us_layer"]},
         "weight_stream_gbs": round(r["weight_gbs"], 1),
         "weight_stream_frac_of_peak": round(r["weight_gbs"] / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
