@@ -113,6 +113,125 @@ def time_gemm(torch, frt, device, synth, M, K, N, dtype, reps=128, pool_bytes=1 
     return us, wbytes + extra, splits
 
 
+def time_sequence(torch, enqueue, ncopy, reps=128):
+    """Mean us per instance of a workload's launch sequence.  `reps` instances replay as one
+    graph, instance i on weight copy i % ncopy (the copies together exceed the last-level
+    cache, so every instance streams its weights from HBM); HIP events on the replay stream
+    bracket the replay."""
+    stream = torch.cuda.current_stream()
+    for i in range(ncopy):
+        enqueue(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream().cuda_stream
+        for i in range(reps):
+            enqueue(i, cap)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del graph
+    return us
+
+
+def stand_alone_workloads(torch, frt, device, synth, pool_bytes=1 << 30):
+    """The stand-alone workloads as their configurations compose them, each timed with cold
+    weights: (1) residual + RMSNorm producer -> bf16 GEMM M=10, K=N=1024, s in {1, 2, 4},
+    bf16 output; (2) producer -> gate|up GEMM M=50 (1024 -> 8192) with the SiLU gate ->
+    down projection (4096 -> 1024, fp32 partials), s_down in {1, 2, 4, 8}; (3) the FP8 block
+    at M=10: gated residual + AdaRMSNorm -> e4m3, fused QKV (1024 -> 2560, bf16 output),
+    gate|up + SiLU gate -> e4m3, down projection (partials).  Static activation scales are
+    fixed for timing (their values do not change the work)."""
+    T = device.to_dev
+    out = {}
+    # workload 1
+    w1 = synth.workload1()
+    M, K, N, eps = w1["M"], w1["K"], w1["N"], w1["eps"]
+    wp, _ = device.pack_weight(w1["w"], frt.BF16, frt.W_PLAIN, gamma=w1["gamma"])
+    pool = [wp.clone() for _ in range(max(8, pool_bytes // wp.numel() + 1))]
+    x, r = T(w1["x"][None]), T(w1["r"])
+    h = device.empty_f32(M, K)
+    op = device.empty_bytes(frt.frt_operand_bytes(frt.BF16, M, K))
+    y = device.empty_bytes(M * N * 2)
+    parts = device.empty_f32(4, M, N)
+    for s_ in (1, 2, 4):
+        def enq(i, st, s_=s_):
+            frt.frt_residual_norm_quant(M, K, x, 1, 1.0, None, r, h, None, None, None, eps, frt.BF16, 1.0, op,
+                                        stream=st)
+            frt.frt_skinny_gemm_splitk(M, N, K, s_, frt.BF16, frt.W_PLAIN, op, pool[i % len(pool)], None, 1.0,
+                                       parts, parts.numel() * 4, frt.EPI_STORE_BF16, y, frt.BF16, 1.0, stream=st)
+        us = time_sequence(torch, enq, len(pool))
+        out[f"w1_rmsnorm_gemm_m10_1024x1024_bf16_s{s_}"] = dict(
+            us=round(us, 3), weight_bytes=K * N * 2, weight_gbs=round(K * N * 2 / (us * 1e-6) / 1e9, 1))
+    del pool
+    # workload 2
+    w2 = synth.workload2()
+    M, K, Fm, eps = w2["M"], w2["K"], w2["mlp"], w2["eps"]
+    wu, _ = device.pack_weight(w2["w_up"], frt.BF16, frt.W_GATE_UP)
+    wd, _ = device.pack_weight(w2["w_down"], frt.BF16, frt.W_PLAIN)
+    ncopy = max(8, pool_bytes // (wu.numel() + wd.numel()) + 1)
+    pu, pd = [wu.clone() for _ in range(ncopy)], [wd.clone() for _ in range(ncopy)]
+    x, r = T(w2["x"][None]), T(w2["r"])
+    h = device.empty_f32(M, K)
+    op = device.empty_bytes(frt.frt_operand_bytes(frt.BF16, M, K))
+    z = device.empty_bytes(frt.frt_operand_bytes(frt.BF16, M, Fm))
+    parts = device.empty_f32(8, M, K)
+    wbytes = K * 2 * Fm * 2 + Fm * K * 2
+    for s_ in (1, 2, 4, 8):
+        def enq(i, st, s_=s_):
+            frt.frt_residual_norm_quant(M, K, x, 1, 1.0, None, r, h, None, None, None, eps, frt.BF16, 1.0, op,
+                                        stream=st)
+            frt.frt_skinny_gemm_splitk(M, 2 * Fm, K, 1, frt.BF16, frt.W_GATE_UP, op, pu[i % ncopy], None, 1.0,
+                                       None, 0, frt.EPI_SILU_GATE_QUANT, z, frt.BF16, 1.0, stream=st)
+            frt.frt_skinny_gemm_splitk(M, K, Fm, s_, frt.BF16, frt.W_PLAIN, z, pd[i % ncopy], None, 1.0,
+                                       parts, parts.numel() * 4, frt.EPI_NONE, None, frt.BF16, 1.0, stream=st)
+        us = time_sequence(torch, enq, ncopy)
+        out[f"w2_gated_mlp_m50_bf16_sdown{s_}"] = dict(
+            us=round(us, 3), weight_bytes=wbytes, weight_gbs=round(wbytes / (us * 1e-6) / 1e9, 1))
+    del pu, pd
+    # workload 3
+    w3 = synth.workload3()
+    M, K, Fm, NQ, eps = w3["M"], w3["K"], w3["mlp"], w3["n_qkv"], w3["eps"]
+    E = frt.E4M3
+    wq, cq = device.pack_weight(w3["w_qkv"], E, frt.W_PLAIN)
+    wu, cu = device.pack_weight(w3["w_up"], E, frt.W_GATE_UP)
+    wd, cd = device.pack_weight(w3["w_down"], E, frt.W_PLAIN)
+    per = wq.numel() + wu.numel() + wd.numel()
+    ncopy = max(8, pool_bytes // per + 1)
+    pq, pu, pd = ([t.clone() for _ in range(ncopy)] for t in (wq, wu, wd))
+    x, r = T(w3["x"][None]), T(w3["r"])
+    sc, sh, gt = (T(w3["mod"][i]) for i in range(3))
+    h = device.empty_f32(M, K)
+    op = device.empty_bytes(frt.frt_operand_bytes(E, M, K))
+    qkv = device.empty_bytes(M * NQ * 2)
+    z = device.empty_bytes(frt.frt_operand_bytes(E, M, Fm))
+    s_dn = frt.frt_splitk_choose(M, K, Fm, E)
+    parts = device.empty_f32(s_dn, M, K)
+    s_y, s_z = 8.0 / 448.0, 16.0 / 448.0
+
+    def enq(i, st):
+        frt.frt_residual_norm_quant(M, K, x, 1, 1.0, None, r, h, gt, sc, sh, eps, E, s_y, op, stream=st)
+        frt.frt_skinny_gemm_splitk(M, NQ, K, 1, E, frt.W_PLAIN, op, pq[i % ncopy], cq, s_y, None, 0,
+                                   frt.EPI_STORE_BF16, qkv, frt.BF16, 1.0, stream=st)
+        frt.frt_skinny_gemm_splitk(M, 2 * Fm, K, 1, E, frt.W_GATE_UP, op, pu[i % ncopy], cu, s_y, None, 0,
+                                   frt.EPI_SILU_GATE_QUANT, z, E, s_z, stream=st)
+        frt.frt_skinny_gemm_splitk(M, K, Fm, s_dn, E, frt.W_PLAIN, z, pd[i % ncopy], cd, s_z, parts,
+                                   parts.numel() * 4, frt.EPI_NONE, None, E, 1.0, stream=st)
+    us = time_sequence(torch, enq, ncopy)
+    wbytes = per + 4 * (NQ + 2 * Fm + K)
+    out[f"w3_fp8_block_m10_e4m3_sdown{s_dn}"] = dict(
+        us=round(us, 3), weight_bytes=wbytes, weight_gbs=round(wbytes / (us * 1e-6) / 1e9, 1))
+    del pq, pu, pd
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_dominant_gemm(torch, frt, device, synth, dims, dtype, reps=128):
     """The gate|up GEMM of one action-decoder layer (M x hidden x 2*mlp)."""
     return time_gemm(torch, frt, device, synth, dims["M"], dims["hidden"], 2 * dims["mlp"], dtype, reps)
@@ -318,6 +437,9 @@ def main():
     ap.add_argument("--dominant-only", action="store_true",
                     help="run only the dominant GEMM's timed graph and a plain copy of known size "
                          "(the program the HBM-traffic counter passes profile)")
+    ap.add_argument("--workloads", action="store_true",
+                    help="time only the stand-alone workloads (fused RMSNorm + GEMM, gated MLP, FP8 block) "
+                         "with cold weights and print them as one JSON line")
     ap.add_argument("--chain-only", action="store_true",
                     help="run only the M=50 bf16 chain (read-ahead on) for --warmup + --steps decisions "
                          "(the program the launch-gap kernel trace profiles)")
@@ -333,6 +455,10 @@ def main():
     from gemm_chains_amd import chain, device, frt
     frt.lib()
     torch.cuda.set_device(0)
+
+    if args.workloads:
+        print(json.dumps(stand_alone_workloads(torch, frt, device, synth)), flush=True)
+        return
 
     if args.chain_only:
         dims = synth.chain_dims(layers=args.layers, steps=args.flow_steps, M=50)
