@@ -395,15 +395,17 @@ def measured_traffic():
     return int(fields["traffic_bytes_per_launch"].strip())
 
 
-def cpu_baseline(synth, dims_full, budget_s=12.0):
+def cpu_baseline(synth, dims_full, budget_s=12.0, single_budget_s=6.0):
     """The float64 oracle on a bounded sample of the same workload: all 18 layers of the
-    first flow steps, as many steps as fit the budget (at least one)."""
+    first flow steps, as many steps as fit the budget (at least one); on all the host's
+    BLAS threads, then again on one thread."""
     import numpy as np
     from oracle import codec, ref
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
+        threadpool_limits = None
         cores = os.cpu_count() or 1
     dims = dict(dims_full)
     dims["steps"] = 1
@@ -411,19 +413,29 @@ def cpu_baseline(synth, dims_full, budget_s=12.0):
     ws = [{n: codec.bf16_decode(l[n]) for n in ("qkv", "o", "up", "down")} for l in wl["layers"]]
     kp = [codec.bf16_decode(l["k_prefix"]) for l in wl["layers"]]
     vp = [codec.bf16_decode(l["v_prefix"]) for l in wl["layers"]]
-    layers_done = 0
-    t0 = time.perf_counter()
-    h, xp, gp = wl["x0"].astype(np.float64), None, None
-    while True:
-        for l in range(dims["layers"]):
-            h, xp, gp = ref.layer(h, xp, gp, wl["mod"][0, l, 0], wl["mod"][0, l, 1], ws[l], np.ones(4),
-                                  kp[l], vp[l], dims, "bf16", 1e-6)
-            layers_done += 1
-        if time.perf_counter() - t0 >= budget_s or layers_done >= 50 * dims["layers"]:
-            break
-    dt = time.perf_counter() - t0
-    return dict(value=round(dt / layers_done * 1e6, 1), unit="us/layer", cores=int(cores), kind="oracle",
-                sample=f"{layers_done} layer applications (M={dims['M']}, bf16, float64 NumPy) in {dt:.1f} s")
+
+    def sample(budget):
+        layers_done = 0
+        t0 = time.perf_counter()
+        h, xp, gp = wl["x0"].astype(np.float64), None, None
+        while True:
+            for l in range(dims["layers"]):
+                h, xp, gp = ref.layer(h, xp, gp, wl["mod"][0, l, 0], wl["mod"][0, l, 1], ws[l], np.ones(4),
+                                      kp[l], vp[l], dims, "bf16", 1e-6)
+                layers_done += 1
+            if time.perf_counter() - t0 >= budget or layers_done >= 50 * dims["layers"]:
+                break
+        dt = time.perf_counter() - t0
+        return dt / layers_done * 1e6, (f"{layers_done} layer applications (M={dims['M']}, bf16, float64 NumPy) "
+                                        f"in {dt:.1f} s")
+
+    us, what = sample(budget_s)
+    out = dict(value=round(us, 1), unit="us/layer", cores=int(cores), kind="oracle", sample=what)
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            us1, what1 = sample(single_budget_s)
+        out["single_thread"] = dict(value=round(us1, 1), unit="us/layer", cores=1, sample=what1)
+    return out
 
 
 def main():
