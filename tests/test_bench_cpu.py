@@ -36,3 +36,11 @@ def test_source_hash_follows_code(sources):
         f.write("\nnamespace frt { constexpr int kUnused = 1; }\n")
     assert bench.gemm_source_hash() != h0
 
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
