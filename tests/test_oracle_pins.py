@@ -464,6 +464,83 @@ def test_calibration_scales_cover_the_calibration_run():
     assert sc[0, 0] >= float(np.float32(np.max(np.abs(y)) / 448.0))
 
 
+def _calibration_by_hand(x0, weights, kp, vp, mod, nh, hd, eps):
+    """The un-quantised chain walked element by element in plain Python (no oracle
+    function but the pinned bf16 rounding of the stored Q, K, V): max |GEMM input| per
+    (layer, site) over every flow step, over 448."""
+    M, H = len(x0), len(x0[0])
+    L, S, nq = len(weights), len(mod), nh * hd
+
+    def matvec(row, W):
+        return [sum(row[k] * W[k][n] for k in range(len(row))) for n in range(len(W[0]))]
+
+    def ada(hrow, sc, sh):
+        rms = math.sqrt(sum(v * v for v in hrow) / len(hrow) + eps)
+        return [hrow[k] / rms * (1.0 + sc[k]) + sh[k] for k in range(len(hrow))]
+
+    def b16(v):
+        return float(codec.bf16_round(np.array([v]))[0])
+
+    amax = [[0.0] * 4 for _ in range(L)]
+    h = [[float(v) for v in row] for row in x0]
+    x_prev = g_prev = None
+    for s in range(S):
+        for l in range(L):
+            w = weights[l]
+            if x_prev is not None:
+                h = [[h[m][k] + g_prev[k] * x_prev[m][k] for k in range(H)] for m in range(M)]
+            y = [ada(h[m], mod[s][l][0][0], mod[s][l][0][1]) for m in range(M)]
+            amax[l][0] = max([amax[l][0]] + [abs(v) for r in y for v in r])
+            c = [matvec(y[m], w["qkv"]) for m in range(M)]
+            keys = [list(r) for r in kp[l]] + [[b16(c[m][nq + e]) for e in range(hd)] for m in range(M)]
+            vals = [list(r) for r in vp[l]] + [[b16(c[m][nq + hd + e]) for e in range(hd)] for m in range(M)]
+            o = [[0.0] * nq for _ in range(M)]
+            for m in range(M):
+                for hh in range(nh):
+                    qv = [b16(c[m][hh * hd + e]) for e in range(hd)]
+                    sc = [sum(qv[e] * kt[e] for e in range(hd)) / math.sqrt(hd) for kt in keys]
+                    top = max(sc)
+                    p = [math.exp(v - top) for v in sc]
+                    for e in range(hd):
+                        o[m][hh * hd + e] = sum(p[t] * vals[t][e] for t in range(len(p))) / sum(p)
+            amax[l][1] = max([amax[l][1]] + [abs(v) for r in o for v in r])
+            xa = [matvec(o[m], w["o"]) for m in range(M)]
+            h = [[h[m][k] + mod[s][l][0][2][k] * xa[m][k] for k in range(H)] for m in range(M)]
+            y2 = [ada(h[m], mod[s][l][1][0], mod[s][l][1][1]) for m in range(M)]
+            amax[l][2] = max([amax[l][2]] + [abs(v) for r in y2 for v in r])
+            F = len(w["up"][0]) // 2
+            z = []
+            for m in range(M):
+                cu = matvec(y2[m], w["up"])
+                z.append([cu[n] / (1.0 + math.exp(-cu[n])) * cu[F + n] for n in range(F)])
+            amax[l][3] = max([amax[l][3]] + [abs(v) for r in z for v in r])
+            x_prev = [matvec(z[m], w["down"]) for m in range(M)]
+            g_prev = mod[s][l][1][2]
+    return np.array(amax) / 448.0
+
+
+def test_chain_calibration_matches_brute_force():
+    """ref.calibrate on a tiny 2-layer x 2-step chain against the hand loop above.  The
+    second flow step's modulation is larger, so every site's maximum comes from it (a
+    calibration that looks at the first step only is caught), and the scales must be the
+    float32 roundings of max/448 (OCP E4M3's largest finite value, not FNUZ's 240)."""
+    x0, weights, _, kp, vp, mod, dims = _tiny_chain_inputs("bf16")
+    master = [{n: w[n] for n in ("qkv", "o", "up", "down")} for w in weights]
+    mod = mod.copy()
+    mod[1] *= 3.0
+    got = ref.calibrate(x0, master, kp, vp, mod, dims, 1e-6)
+    want = _calibration_by_hand(x0.tolist(), [{n: w[n].tolist() for n in w} for w in master],
+                                [k.tolist() for k in kp], [v.tolist() for v in vp], mod.tolist(),
+                                dims["n_heads"], dims["head_dim"], 1e-6)
+    first = _calibration_by_hand(x0.tolist(), [{n: w[n].tolist() for n in w} for w in master],
+                                 [k.tolist() for k in kp], [v.tolist() for v in vp], mod[:1].tolist(),
+                                 dims["n_heads"], dims["head_dim"], 1e-6)
+    assert np.all(want > first * 1.01), "every site's maximum comes from the second step"
+    assert got.shape == want.shape
+    assert np.all(np.abs(got - want) <= 2.0 ** -23 * want + 1e-300)
+    assert np.array_equal(got, got.astype(np.float32).astype(np.float64))
+
+
 def test_block_calibration_is_the_largest_magnitude_over_448():
     # brute force on a tiny block: walk every element of the un-quantised run by hand
     rng = np.random.default_rng(5)
@@ -546,6 +623,18 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         X = np_.ldexp(1.0, e)
         return codec.fp4_encode(b / X[:, None, :]).reshape(K, N), (e + 127).astype(np_.uint8), X
     _planted(monkeypatch, codec, "mxfp4_encode", mx_emax3, test_mxfp4_block_scales)
+    with monkeypatch.context() as m:                                        # FNUZ's 240 for 448
+        m.setattr(codec, "E4M3_MAX", 240.0)
+        with pytest.raises(AssertionError):
+            test_chain_calibration_matches_brute_force()
+    orig_cal = ref.calibrate
+    _planted(monkeypatch, ref, "calibrate",                                 # first flow step only
+             lambda x0, w, kp, vp, mod, dims, eps: orig_cal(x0, w, kp, vp, np_.asarray(mod)[:1], dims, eps),
+             test_chain_calibration_matches_brute_force)
+    _planted(monkeypatch, ref, "calibrate",                                 # last layer's maxima for all
+             lambda x0, w, kp, vp, mod, dims, eps: np_.repeat(orig_cal(x0, w, kp, vp, mod, dims, eps)[-1:],
+                                                              len(w), axis=0),
+             test_chain_calibration_matches_brute_force)
     orig_red = ref.reduce_partials
     _planted(monkeypatch, ref, "reduce_partials",
              lambda p, a=1.0, c=None: orig_red(np_.asarray(p)[:1], a, c),
