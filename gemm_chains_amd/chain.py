@@ -9,6 +9,7 @@ BUFFER_DTYPES = {"x_in": np.float32, "x_out": np.float32, "mod": np.float32, "ac
                  "k_cache": np.int16, "v_cache": np.int16, "h": np.float32,
                  "dbg_h_attn": np.float32, "dbg_h_mlp": np.float32,
                  "dbg_p_o": np.float32, "dbg_p_down": np.float32, "dbg_q": np.int16,
+                 "dbg_k_own": np.int16, "dbg_v_own": np.int16,
                  "dbg_a_qkv": np.uint8, "dbg_a_o": np.uint8, "dbg_a_up": np.uint8, "dbg_a_down": np.uint8}
 _TORCH = {np.float32: torch.float32, np.int16: torch.int16, np.uint8: torch.uint8}
 

@@ -36,7 +36,7 @@ struct ChainLayout {
   size_t pq = 0, po = 0, pu = 0, pd = 0;                   // partial bytes (one copy)
   size_t qb = 0, attn_ws = 0;
   Buf x_in, x_out, mod, act, kc, vc, h, q, aws, sink, amax, a_qkv, a_o, a_up, a_down, p_qkv, p_o, p_up, p_down;
-  Buf d_h_attn, d_h_mlp, d_a_qkv, d_a_o, d_a_up, d_a_down, d_p_o, d_p_down, d_q;
+  Buf d_h_attn, d_h_mlp, d_a_qkv, d_a_o, d_a_up, d_a_down, d_p_o, d_p_down, d_q, d_k, d_v;
   size_t total = 0;
 };
 
@@ -147,6 +147,8 @@ static int make_layout(const frt_chain_desc* d, ChainLayout& L) {
     take(L.d_p_o, SL * align256(L.po));
     take(L.d_p_down, SL * align256(L.pd));
     take(L.d_q, SL * align256(L.qb));
+    take(L.d_k, SL * align256((size_t)M * d->head_dim * 2));
+    take(L.d_v, SL * align256((size_t)M * d->head_dim * 2));
   }
   L.total = off;
   return FRT_OK;
@@ -170,6 +172,19 @@ struct frt_chain {
 
 static uint8_t* at(frt_chain* c, const Buf& b, size_t idx = 0, size_t stride = 0) {
   return c->arena + b.off + idx * stride;
+}
+
+// Debug chains only: copy the own key rows [M][hd] of one layer's key cache and its own
+// value columns of the transposed value cache ([hd][ldv], columns 0..M-1 from vt) into
+// per-(step, layer) buffers, both row-major [M][hd], before the next flow step rewrites
+// them.
+__global__ void copy_own_kv_kernel(const uint16_t* __restrict__ k_own, const uint16_t* __restrict__ vt, int ldv,
+                                   int M, int hd, uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * hd) return;
+  k_dst[i] = k_own[i];
+  const int m = i / hd, e = i - m * hd;
+  v_dst[i] = vt[(size_t)e * ldv + m];
 }
 
 // Enqueue the whole chain on `s` (eager launches; also what graph capture records).
@@ -280,6 +295,15 @@ static int enqueue_chain(frt_chain* c, hipStream_t s, int* count, unsigned* amax
         r.act_scale = 1.f; r.act_scale_ptr = actp(l, SITE_QKV); r.colscale = gq.colscale; r.epi = kEpiQkv;
         r.q_out = gq.q_out; r.k_out = gq.k_out; r.v_out = gq.v_out; r.nq = gq.nq; r.hd = gq.hd; r.v_ld = gq.v_ld;
         FRT_HIP(launch_reduce(r, s)); ++n;
+      }
+
+      if (dbg) {  // keep this step's own K/V rows for inspection
+        const int nkv = M * d.head_dim;
+        const size_t kvb = align256((size_t)nkv * 2);
+        hipLaunchKernelGGL(copy_own_kv_kernel, dim3((nkv + 255) / 256), dim3(256), 0, s,
+                           (const uint16_t*)gq.k_out, (const uint16_t*)gq.v_out, L.ldv, M, d.head_dim,
+                           (uint16_t*)at(c, L.d_k, idx, kvb), (uint16_t*)at(c, L.d_v, idx, kvb));
+        FRT_HIP(hipGetLastError()); ++n;
       }
 
       // 3. attention over [prefix ; own rows] -> O-projection operand
@@ -422,7 +446,7 @@ extern "C" int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_de
   } else {
     // count the launches without enqueueing anything
     const int attn_o = c->L.fuse_o ? 2 : attention_kernel_count(c->d.M, c->d.n_heads, c->L.kv_len) + 1;
-    const int per_layer = 5 + attn_o + (c->L.s_up > 1) + (c->L.s_qkv > 1);
+    const int per_layer = 5 + attn_o + (c->L.s_up > 1) + (c->L.s_qkv > 1) + (c->d.keep_intermediates != 0);
     c->kernels = desc->steps * desc->layers * per_layer + 1;
   }
   *out = c;
@@ -437,7 +461,8 @@ extern "C" int frt_layer_chain_buffer(frt_chain* c, const char* name, void** dev
       {"k_cache", &L.kc}, {"v_cache", &L.vc}, {"h", &L.h},
       {"dbg_h_attn", &L.d_h_attn}, {"dbg_h_mlp", &L.d_h_mlp}, {"dbg_a_qkv", &L.d_a_qkv},
       {"dbg_a_o", &L.d_a_o}, {"dbg_a_up", &L.d_a_up}, {"dbg_a_down", &L.d_a_down},
-      {"dbg_p_o", &L.d_p_o}, {"dbg_p_down", &L.d_p_down}, {"dbg_q", &L.d_q}};
+      {"dbg_p_o", &L.d_p_o}, {"dbg_p_down", &L.d_p_down}, {"dbg_q", &L.d_q},
+      {"dbg_k_own", &L.d_k}, {"dbg_v_own", &L.d_v}};
   for (const Named& t : tab) {
     if (strcmp(t.n, name) == 0) {
       if (t.b->bytes == 0) return FRT_E_STATE;
@@ -462,27 +487,68 @@ extern "C" int frt_layer_chain_run(frt_chain* c, void* stream) {
 extern "C" int frt_layer_chain_kernel_count(const frt_chain* c) { return c ? c->kernels : -1; }
 
 // The persistent state is the arena's leading region, up to the first working buffer.
-extern "C" size_t frt_layer_chain_state_bytes(const frt_chain* c) { return c ? c->L.h.off : 0; }
+// A capsule holds that region followed by a 256-byte trailer whose first 16 bytes are a
+// magic word and a token of the chain's shape fields and state layout, so a capsule is
+// restored only into a chain whose state it fits.
+constexpr size_t kTrailer = 256;
+constexpr uint64_t kCapsuleMagic = 0x31555350'41435446ull;  // "FTCAPSU1" little-endian
 
-static int state_copy(frt_chain* c, void* stream, void* dst, const void* src, const void* capsule, size_t bytes) {
+static uint64_t layout_token(const frt_chain* c) {
+  const frt_chain_desc& d = c->d;
+  const ChainLayout& L = c->L;
+  const uint64_t f[] = {(uint64_t)d.layers, (uint64_t)d.steps, (uint64_t)d.M, (uint64_t)d.hidden,
+                        (uint64_t)d.n_heads, (uint64_t)d.head_dim, (uint64_t)d.prefix_len, (uint64_t)d.mlp,
+                        (uint64_t)act_dtype_of(d.dtype), L.x_in.off, L.x_out.off, L.mod.off, L.act.off, L.kc.off,
+                        L.vc.off, L.h.off};
+  uint64_t h = 1469598103934665603ull;  // FNV-1a over the fields' bytes
+  for (uint64_t v : f)
+    for (int b = 0; b < 8; ++b) h = (h ^ ((v >> (8 * b)) & 0xffu)) * 1099511628211ull;
+  return h;
+}
+
+__global__ void write_trailer_kernel(uint64_t* dst, uint64_t magic, uint64_t token) {
+  if (threadIdx.x == 0) {
+    dst[0] = magic;
+    dst[1] = token;
+  }
+}
+
+extern "C" size_t frt_layer_chain_state_bytes(const frt_chain* c) { return c ? c->L.h.off + kTrailer : 0; }
+
+static int capsule_args(frt_chain* c, const void* capsule, size_t bytes) {
   FRT_CHECK(c, FRT_E_STATE);
   FRT_CHECK(capsule, FRT_E_NULL);
   FRT_CHECK(aligned16(capsule), FRT_E_ALIGN);
-  const size_t n = c->L.h.off;
-  FRT_CHECK(bytes >= n, FRT_E_WORKSPACE);
-  FRT_CHECK(!overlaps(capsule, n, c->arena, c->arena_bytes), FRT_E_ALIAS);
-  FRT_HIP(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, (hipStream_t)stream));
+  FRT_CHECK(bytes == c->L.h.off + kTrailer, FRT_E_WORKSPACE);
+  FRT_CHECK(!overlaps(capsule, bytes, c->arena, c->arena_bytes), FRT_E_ALIAS);
   return FRT_OK;
 }
 
 extern "C" int frt_layer_chain_snapshot(frt_chain* c, void* stream, void* capsule_dev, size_t capsule_bytes) {
-  if (!c) return FRT_E_STATE;
-  return state_copy(c, stream, capsule_dev, c->arena, capsule_dev, capsule_bytes);
+  const int st = capsule_args(c, capsule_dev, capsule_bytes);
+  if (st) return st;
+  const size_t n = c->L.h.off;
+  hipStream_t s = (hipStream_t)stream;
+  FRT_HIP(hipMemcpyAsync(capsule_dev, c->arena, n, hipMemcpyDeviceToDevice, s));
+  hipLaunchKernelGGL(write_trailer_kernel, dim3(1), dim3(64), 0, s, (uint64_t*)((uint8_t*)capsule_dev + n),
+                     kCapsuleMagic, layout_token(c));
+  FRT_HIP(hipGetLastError());
+  return FRT_OK;
 }
 
 extern "C" int frt_layer_chain_restore(frt_chain* c, void* stream, const void* capsule_dev, size_t capsule_bytes) {
-  if (!c) return FRT_E_STATE;
-  return state_copy(c, stream, c->arena, capsule_dev, capsule_dev, capsule_bytes);
+  const int st = capsule_args(c, capsule_dev, capsule_bytes);
+  if (st) return st;
+  const size_t n = c->L.h.off;
+  hipStream_t s = (hipStream_t)stream;
+  // the trailer is read back after whatever the stream already holds (the capsule may
+  // have been written by work queued there), then checked on the host
+  uint64_t trailer[2] = {0, 0};
+  FRT_HIP(hipMemcpyAsync(trailer, (const uint8_t*)capsule_dev + n, sizeof trailer, hipMemcpyDeviceToHost, s));
+  FRT_HIP(hipStreamSynchronize(s));
+  FRT_CHECK(trailer[0] == kCapsuleMagic && trailer[1] == layout_token(c), FRT_E_STATE);
+  FRT_HIP(hipMemcpyAsync(c->arena, capsule_dev, n, hipMemcpyDeviceToDevice, s));
+  return FRT_OK;
 }
 
 __global__ void amax_to_scale_kernel(const unsigned* amax, float* scales, int n) {

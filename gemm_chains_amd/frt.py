@@ -8,7 +8,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfrt.so")
+# the in-tree build; FRT_LIBRARY names another build of the same sources (the host-side
+# sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("FRT_LIBRARY") or os.path.join(_HERE, "libfrt.so")
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_SPLITK, E_WORKSPACE, E_ALIAS, E_STATE, E_HIP, E_ARG = range(11)
 BF16, E4M3, F32, MXFP4 = 1, 2, 3, 4
@@ -51,6 +53,7 @@ _SIGS = {
     "frt_status_string": (ctypes.c_char_p, [_int]),
     "frt_last_hip_error": (_int, []),
     "frt_version": (_int, []),
+    "frt_diag_empty_kernels": (_int, [_c_void_p, _int, _int]),
     "frt_operand_bytes": (_size, [_int, _int, _int]),
     "frt_weight_bytes": (_size, [_int, _int, _int]),
     "frt_operand_pack_host": (_int, [_c_void_p, _int, _int, _int, _c_void_p]),
@@ -133,6 +136,10 @@ def _stream(stream):
 def _check(status, where):
     if status != OK:
         raise FrtError(status, where)
+
+
+def frt_diag_empty_kernels(n, workgroups, stream=None):
+    _check(_lib().frt_diag_empty_kernels(_stream(stream), n, workgroups), "frt_diag_empty_kernels")
 
 
 # ------------------------------------------------------------------ layout helpers

@@ -84,6 +84,12 @@ typedef enum {
 const char* frt_status_string(int status);
 int frt_last_hip_error(void);      /* hipError_t of this thread's last FRT_E_HIP, else 0 */
 int frt_version(void);             /* 100 * major + minor                                */
+/* Enqueue n empty kernels of `workgroups` x 256 threads on `stream` (nothing is read or
+ * written): the cost of a dependent launch before any work, for the launch-overlap
+ * measurements (pages: rebasdaily FlashRT-PAI news summary, section "快内核为什么拼不出快
+ * 管线？": the gaps between kernels are part of the pipeline's time).  Capturable into a
+ * graph.  0 <= n <= 100000, 1 <= workgroups <= 65536, else FRT_E_ARG.                  */
+int frt_diag_empty_kernels(void* stream, int n, int workgroups);
 
 /* ------------------------------------------------------------------ layouts */
 /* Bytes of a packed GEMM operand (A) holding M x K values: Mp * K * (2 | 1). */
@@ -298,9 +304,12 @@ int frt_layer_chain_create(const frt_chain_desc* desc, void* arena_dev, size_t a
  *   "h"         [M][hidden] fp32   working residual stream (not kept per layer)
  *   debug (keep_intermediates): "dbg_h_attn", "dbg_h_mlp" [steps][layers][M][hidden] fp32,
  *   "dbg_a_qkv", "dbg_a_o", "dbg_a_up", "dbg_a_down" [steps][layers] packed operands,
- *   "dbg_p_o", "dbg_p_down" [steps][layers][splits][M][N] fp32 and "dbg_q"
- *   [steps][layers][M][n_heads*head_dim] bf16; each (step, layer) slice starts on a
- *   256-byte boundary.  A name whose buffer is empty returns FRT_E_STATE.              */
+ *   "dbg_p_o", "dbg_p_down" [steps][layers][splits][M][N] fp32, "dbg_q"
+ *   [steps][layers][M][n_heads*head_dim] bf16, and "dbg_k_own", "dbg_v_own"
+ *   [steps][layers][M][head_dim] bf16 (each layer-step's own key and value rows, copied
+ *   out of the caches by one extra kernel per layer before the next step rewrites them);
+ *   each (step, layer) slice starts on a 256-byte boundary.  A name whose buffer is
+ *   empty returns FRT_E_STATE.                                                         */
 int frt_layer_chain_buffer(frt_chain* chain, const char* name, void** dev, size_t* bytes);
 /* Static activation scales for an e4m3 chain built from the same bf16 master weights:
  * runs this bf16 chain once, eagerly, on the current "x_in" / "mod" / caches (the
@@ -315,14 +324,22 @@ int frt_layer_chain_calibrate(frt_chain* chain, void* stream, float* scales_dev)
 /* Execution-state capsule (abstract page, "execution-state capsule": the state a
  * decision runs on is captured as a unit that can be restored or forked).  The chain's
  * persistent state -- "x_in", "x_out", "mod", "act_scale", "k_cache", "v_cache" -- is the
- * leading region of the arena, so a capsule is one device copy of state_bytes bytes:
- *   snapshot: chain state -> capsule_dev;  restore: capsule_dev -> chain state.
- * A capsule restores into any chain created with the same shape fields (layers, steps,
- * M, hidden, n_heads, head_dim, prefix_len, mlp, dtype); restoring it into a second
- * chain forks the state (that chain may hold other weights).  The copy is queued on
- * `stream` (asynchronous); capsule_dev is caller-owned device memory, 16-byte aligned,
- * >= state_bytes, and must not overlap the arena (FRT_E_ALIAS).  The rest of the arena
- * (working buffers) is rewritten by every run and is not part of the state.           */
+ * leading region of the arena.  A capsule is that region followed by a 256-byte trailer
+ * (a magic word and a token of the chain's shape fields and state layout); state_bytes
+ * counts both.
+ *   snapshot: chain state -> capsule_dev, then the trailer (queued on `stream`,
+ *             asynchronous);
+ *   restore:  reads the capsule's trailer back after the work already queued on
+ *             `stream`, waits for it (synchronous with the host, so not capturable), and
+ *             returns FRT_E_STATE unless the capsule was written by a chain with the same
+ *             shape fields (layers, steps, M, hidden, n_heads, head_dim, prefix_len, mlp,
+ *             activation format: bf16, or e4m3 for e4m3 and MXFP4 weights); then queues
+ *             the copy capsule_dev -> chain state on `stream`.
+ * Restoring a capsule into a second chain of the same shape forks the state (that chain
+ * may hold other weights).  capsule_dev is caller-owned device memory, 16-byte aligned,
+ * exactly state_bytes long (FRT_E_WORKSPACE otherwise), and must not overlap the arena
+ * (FRT_E_ALIAS).  The rest of the arena (working buffers) is rewritten by every run and
+ * is not part of the state.                                                           */
 size_t frt_layer_chain_state_bytes(const frt_chain* chain);
 int frt_layer_chain_snapshot(frt_chain* chain, void* stream, void* capsule_dev, size_t capsule_bytes);
 int frt_layer_chain_restore(frt_chain* chain, void* stream, const void* capsule_dev, size_t capsule_bytes);

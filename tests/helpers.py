@@ -71,3 +71,38 @@ def silu_gate_mag(c, a_dec, w_dec, act, s_w, dtype, out_scale):
     gte, up = c[:, :n2], c[:, n2:]
     mag = 1.1 * np.abs(up) * g_mag[:, :n2] + np.abs(ref.silu(gte)) * g_mag[:, n2:] + np.abs(ref.silu(gte) * up)
     return mag / out_scale if dtype == "e4m3" else mag
+
+
+class Canaries:
+    """Device buffers with PAD canary bytes on each side (SURVEY's canary-guarded outputs):
+    `bytes` / `f32` hand out the inner region, `check` asserts that no kernel wrote past
+    either end of any buffer handed out."""
+    PAD = 256
+    BYTE = 0x5A
+
+    def __init__(self):
+        self.bufs = []
+
+    def bytes(self, nbytes):
+        import torch
+        n = max(int(nbytes), 16)
+        buf = torch.full((n + 2 * self.PAD,), self.BYTE, dtype=torch.uint8, device="cuda")
+        self.bufs.append((buf, n))
+        return buf[self.PAD:self.PAD + n]
+
+    def f32(self, *shape):
+        import torch
+        n = int(np.prod(shape)) * 4
+        buf = torch.full((n + 2 * self.PAD,), self.BYTE, dtype=torch.uint8, device="cuda")
+        self.bufs.append((buf, n))
+        return buf[self.PAD:self.PAD + n].view(torch.float32).view(*shape)
+
+    def check(self):
+        import torch
+        torch.cuda.synchronize()
+        for i, (buf, n) in enumerate(self.bufs):
+            head = buf[:self.PAD].cpu().numpy()
+            tail = buf[self.PAD + n:].cpu().numpy()
+            assert np.all(head == self.BYTE), f"buffer {i} ({n} bytes): canary before it overwritten"
+            assert np.all(tail == self.BYTE), f"buffer {i} ({n} bytes): canary after it overwritten"
+        return len(self.bufs)

@@ -14,11 +14,14 @@ the same seeded inputs (it never reads a GPU output).  Bars:
   - operand codes: the tie band (tests/helpers.py); packed weights: bit-exact;
   - GEMM outputs (the reduced, scale-recovered fp32 C): relative L2 <= 5e-3 (bf16) and
     <= 2e-3 (e4m3) against the oracle's quantisation-emulating path; split-K against
-    unsplit on the GPU <= 1e-5 (bf16) / 1e-4 (e4m3);
+    unsplit on the GPU <= 1e-5 (bf16 and e4m3);
   - codes that a GEMM epilogue rounds (the SiLU-gate output) are checked teacher-forced:
     the GPU GEMM is fed the oracle's operand codes (host-packed) and its codes must match
     up to the tie band; end to end (on the GPU's own operand) their decoded values must
-    stay within the GEMM-output bar.
+    stay within the GEMM-output bar, except in the FP8 block, where one-step flips of
+    downstream e4m3 codes that the tie band allows dominate: there the end-to-end bar is
+    twice the oracle's own sensitivity (2^-17 relative noise on the producer's values),
+    and the test prints whether the stated 2e-3 is met.
 """
 import math
 
@@ -30,7 +33,7 @@ import synth
 from oracle import codec, ref
 from tests.helpers import check_codes, rel_l2, silu_gate_mag
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("canaries")]
 
 
 @pytest.fixture(scope="module")
@@ -106,7 +109,7 @@ def test_config1_fused_rmsnorm_bf16_gemm(F):
     outs = {}
     for s in (1, 2, 4):
         c = _gemm_f32(frt, dev, M, N, K, s, frt.BF16, frt.W_PLAIN, op, wp, None, 1.0)
-        cb = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        cb = dev.empty_bytes(M * N * 2).view(torch.int16).view(M, N)
         parts = dev.empty_f32(s, M, N)
         frt.frt_skinny_gemm_splitk(M, N, K, s, frt.BF16, frt.W_PLAIN, op, wp, None, 1.0, parts, parts.numel() * 4,
                                    frt.EPI_STORE_BF16, cb, frt.BF16, 1.0)
@@ -205,7 +208,7 @@ def test_config3_fp8_static_scale_block(F):
         assert rel_l2(qkv[s], c_qkv) <= 2e-3, f"qkv s={s}"
         print(f"config 3 qkv s={s}: rel L2 {rel_l2(qkv[s], c_qkv):.2e}")
     for s in (2, 4, 8):
-        assert rel_l2(qkv[s], qkv[1]) <= 1e-4
+        assert rel_l2(qkv[s], qkv[1]) <= 1e-5, f"qkv split {s} vs unsplit"
     _silu_teacher_forced(frt, dev, M, 2 * Fm, K, 1, E, "e4m3", o, wu, cu, dec(uc), us, s_y, s_z, "config 3 SiLU")
     zo = _silu(frt, dev, M, 2 * Fm, K, 1, E, op, wu, cu, s_y, s_z)
     torch.cuda.synchronize()
@@ -227,8 +230,14 @@ def test_config3_fp8_static_scale_block(F):
     e2e_z, e2e = rel_l2(dec(zc[:M]), z["deq"]), rel_l2(dev.to_np(c), c_down)
     print(f"config 3 end to end: SiLU output rel L2 {e2e_z:.2e} (oracle sensitivity {sens_z:.2e}), "
           f"down rel L2 {e2e:.2e} (sensitivity {sens_d:.2e})")
-    assert e2e_z <= max(2e-3, 2 * sens_z), "config 3 SiLU end to end"
-    assert e2e <= max(2e-3, 2 * sens_d), "config 3 down end to end"
+    # The stated fp8 bar (2e-3) holds for every GEMM output teacher-forced (above and
+    # below).  End to end, the one-step flips of downstream e4m3 codes that the tie band
+    # allows dominate (about 2.6e-3 measured against 2e-3): that leg passes only under the
+    # sensitivity reading (twice the oracle's own change), and the print says which.
+    print(f"config 3 end to end vs the stated 2e-3: SiLU {'meets' if e2e_z <= 2e-3 else 'MISSES'}, "
+          f"down {'meets' if e2e <= 2e-3 else 'MISSES'}")
+    assert e2e_z <= 2 * sens_z, "config 3 SiLU end to end"
+    assert e2e <= 2 * sens_d, "config 3 down end to end"
     # teacher-forced down projection
     a_pk = dev.to_dev(frt.frt_operand_pack_host(z["codes"], E, M, Fm))
     c = _gemm_f32(frt, dev, M, K, Fm, 4, E, frt.W_PLAIN, a_pk, wd, cd, s_z)

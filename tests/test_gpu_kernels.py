@@ -10,7 +10,7 @@ relative L2 1e-5 of the float64 products for bf16 (fp32 accumulation of exact pr
 and 1e-4 for e4m3 (the 16x16x128 fp8 MFMA sums its 128 exact products with less than
 fp32 precision inside the instruction: ~1.5e-5 measured); bf16 GEMM outputs within
 relative L2 5e-3 and fp8 outputs within 2e-3 of the emulating oracle; split-K against
-unsplit within 1e-5 (bf16) and 1e-4 (e4m3).
+unsplit within 1e-5 (both on the GPU, in fp32: only the order of the k-step sums differs).
 """
 import math
 
@@ -22,7 +22,7 @@ import synth
 from oracle import codec, ref
 from tests.helpers import check_codes, rel_l2, silu_gate_mag
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("canaries")]
 
 
 @pytest.fixture(scope="module")
@@ -210,7 +210,7 @@ def test_gemm_store_epilogues_and_splitk_invariance(F, M, N, K, dtype):
         c32 = dev.empty_f32(M, N)
         frt.frt_skinny_gemm_splitk(M, N, K, s, dt, frt.W_PLAIN, a_pk, w_pk, cs, act, parts, parts.numel() * 4,
                                    frt.EPI_STORE_F32, c32, frt.F32, 1.0)
-        cb = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        cb = dev.empty_bytes(M * N * 2).view(torch.int16).view(M, N)
         frt.frt_skinny_gemm_splitk(M, N, K, s, dt, frt.W_PLAIN, a_pk, w_pk, cs, act, parts, parts.numel() * 4,
                                    frt.EPI_STORE_BF16, cb, frt.BF16, 1.0)
         torch.cuda.synchronize()
@@ -225,7 +225,7 @@ def test_gemm_store_epilogues_and_splitk_invariance(F, M, N, K, dtype):
         check_codes(bits, c_o, g_mag, "bf16", max_frac=0.01 if dtype == "bf16" else 0.05,
                     label=f"bf16 store s={s}")
     for s in outs:
-        assert rel_l2(outs[s], outs[1]) <= (1e-5 if dtype == "bf16" else 1e-4), f"split {s} vs unsplit"
+        assert rel_l2(outs[s], outs[1]) <= 1e-5, f"split {s} vs unsplit"
         print(f"split {s} vs unsplit rel L2 {rel_l2(outs[s], outs[1]):.2e}")
 
 
@@ -268,10 +268,10 @@ def test_qkv_gemm_epilogue(F, M, K, dtype, splits):
     cs = dev.to_dev(s_w.astype(np.float32)) if dtype == "e4m3" else None
     c_o = ref.reduce_partials(ref.gemm_splitk(a_dec, w_dec, 1), act, s_w)
     g_mag = (np.abs(a_dec) @ np.abs(w_dec)) * act * (s_w[None, :] if s_w is not None else 1.0)
-    qo = torch.zeros((M, nh * hd), dtype=torch.int16, device="cuda")
-    kc = torch.zeros((M + 3, hd), dtype=torch.int16, device="cuda")      # rows 3.. as in a key cache
+    qo = dev.empty_bytes(M * nh * hd * 2).view(torch.int16).view(M, nh * hd)
+    kc = dev.empty_bytes((M + 3) * hd * 2).view(torch.int16).view(M + 3, hd).zero_()   # rows 3.. as in a key cache
     ldv = (M + 3 + 31) // 32 * 32
-    vc = torch.zeros((hd, ldv), dtype=torch.int16, device="cuda")        # transposed value cache
+    vc = dev.empty_bytes(hd * ldv * 2).view(torch.int16).view(hd, ldv).zero_()         # transposed value cache
     parts = dev.empty_f32(splits, M, N) if splits > 1 else None
     frt.frt_skinny_gemm_qkv(M, K, nh, hd, splits, dt, a_pk, w_pk, cs, act, parts,
                             0 if parts is None else parts.numel() * 4, qo, kc[3:], vc[:, 3:], ldv)
@@ -301,7 +301,8 @@ def test_attention_parity(F, M, out_dtype, prefix):
     if out_dtype == "e4m3":
         mag = mag / out_scale
     wsb = frt.frt_attention_workspace_bytes(M, nh, hd, T)
-    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda")   # no initial contents needed
+    ws = dev.empty_bytes(wsb)
+    ws.fill_(0x7F)                                                    # no initial contents needed
     ldv = (T + 31) // 32 * 32
     vt = np.full((hd, ldv), 0x7FC0, np.uint16)                        # padding holds NaN: never used
     vt[:, :T] = vb.T

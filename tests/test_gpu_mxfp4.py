@@ -23,7 +23,7 @@ import synth
 from oracle import codec, ref
 from tests.helpers import check_codes, rel_l2, silu_gate_mag
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("canaries")]
 
 
 @pytest.fixture(scope="module")
@@ -130,7 +130,7 @@ def test_mxfp4_gemm_store_and_splitk_invariance(F, M, N, K):
         c32 = dev.empty_f32(M, N)
         frt.frt_skinny_gemm_splitk(M, N, K, s, frt.MXFP4, frt.W_PLAIN, a_pk, w_pk, None, act, parts,
                                    parts.numel() * 4, frt.EPI_STORE_F32, c32, frt.F32, 1.0)
-        cb = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        cb = dev.empty_bytes(M * N * 2).view(torch.int16).view(M, N)
         frt.frt_skinny_gemm_splitk(M, N, K, s, frt.MXFP4, frt.W_PLAIN, a_pk, w_pk, None, act, parts,
                                    parts.numel() * 4, frt.EPI_STORE_BF16, cb, frt.BF16, 1.0)
         torch.cuda.synchronize()
@@ -138,7 +138,7 @@ def test_mxfp4_gemm_store_and_splitk_invariance(F, M, N, K):
         assert rel_l2(outs[s], c_o) <= 1e-4
         check_codes(cb.cpu().numpy().view(np.uint16), c_o, g_mag, "bf16", max_frac=0.05, label=f"bf16 store s={s}")
     for s in outs:
-        assert rel_l2(outs[s], outs[1]) <= 1e-4, f"split {s} vs unsplit"
+        assert rel_l2(outs[s], outs[1]) <= 1e-5, f"split {s} vs unsplit"
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(10, 8192, 1024, 1), (50, 8192, 1024, 1), (50, 8192, 1024, 2),
@@ -175,10 +175,10 @@ def test_mxfp4_qkv_gemm_epilogue(F, M, K, splits):
     act = 0.0625
     c_o = ref.reduce_partials(ref.gemm_splitk(a_dec, w_dec, 1), act, None)
     g_mag = (np.abs(a_dec) @ np.abs(w_dec)) * act
-    qo = torch.zeros((M, nh * hd), dtype=torch.int16, device="cuda")
-    kc = torch.zeros((M, hd), dtype=torch.int16, device="cuda")
+    qo = dev.empty_bytes(M * nh * hd * 2).view(torch.int16).view(M, nh * hd).zero_()
+    kc = dev.empty_bytes(M * hd * 2).view(torch.int16).view(M, hd).zero_()
     ldv = (M + 31) // 32 * 32
-    vc = torch.zeros((hd, ldv), dtype=torch.int16, device="cuda")
+    vc = dev.empty_bytes(hd * ldv * 2).view(torch.int16).view(hd, ldv).zero_()
     parts = dev.empty_f32(splits, M, N) if splits > 1 else None
     frt.frt_skinny_gemm_qkv(M, K, nh, hd, splits, frt.MXFP4, a_pk, w_pk, None, act, parts,
                             0 if parts is None else parts.numel() * 4, qo, kc, vc, ldv)
