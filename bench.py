@@ -81,8 +81,12 @@ def time_gemm(torch, frt, device, synth, M, K, N, dtype, reps=128, pool_bytes=1 
     ncopy = max(8, int(pool_bytes // wbytes) + 1)
     pool = [pk.clone() for _ in range(ncopy)]
     adt = frt.act_dtype(dtype)  # MXFP4 weights take an e4m3 operand
+    # a real activation operand: the producer's RMSNorm of N(0,1) rows (e4m3 with the
+    # scale that maps the largest value to 448)
     a = device.empty_bytes(frt.frt_operand_bytes(adt, M, K))
-    a.zero_()
+    x_act = device.to_dev(synth.normal(synth.TEST_SEED, 6, 1, (M, K)))
+    a_scale = 4.5 / 448.0 if adt == frt.E4M3 else 1.0
+    frt.frt_residual_norm_quant(M, K, None, 1, 1.0, None, x_act, None, None, None, None, 1e-6, adt, a_scale, a)
     out = device.empty_bytes(frt.frt_operand_bytes(adt, M, N // 2))
     splits = 1  # the library's choice for a GEMM that ends in an epilogue
     stream = torch.cuda.current_stream()
@@ -369,10 +373,14 @@ GEMM_SOURCES = [os.path.join(ROOT, "gemm_chains_amd", "csrc", f)
 def gemm_source_hash():
     """Hash of the dominant kernel's sources with comments and blank lines removed, so a
     change of wording does not void the counters, while any change of code does."""
+    return source_hash(GEMM_SOURCES)
+
+
+def source_hash(files):
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in files:
         text = open(f, encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
@@ -393,6 +401,125 @@ def measured_traffic():
     if fields.get("source_sha256", "").strip() != gemm_source_hash():
         return None
     return int(fields["traffic_bytes_per_launch"].strip())
+
+
+def launch_cost(torch, frt, n=256):
+    """Cost of one dependent launch: a graph of n empty kernels (frt_diag_empty_kernels, each
+    waiting for the previous, as the chain's kernels do), replayed and timed with HIP events
+    on the replay stream; microseconds per kernel, for 1, 256 and 512 workgroups."""
+    out = {}
+    stream = torch.cuda.current_stream()
+    for wg in (1, 256, 512):
+        graph = torch.cuda.CUDAGraph()
+        frt.frt_diag_empty_kernels(4, wg, stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            frt.frt_diag_empty_kernels(n, wg, stream=torch.cuda.current_stream().cuda_stream)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        best = 1e30
+        for _ in range(5):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / n)
+        out[f"workgroups_{wg}"] = round(best, 3)
+        del graph
+    return out
+
+
+def library_gemm_context(torch, M=50, pool_bytes=1 << 30, reps=64):
+    """torch.matmul (the vendor BLAS) in bf16 at the chain's four GEMM shapes, cold weights
+    (a rotated pool of >= 1 GiB), replayed as a graph and timed with HIP events: context
+    for the skinny GEMM, not part of the path (no norm, quantisation or fused epilogue)."""
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, K, N in (("qkv", 1024, 1280), ("o", 1024, 1024), ("gate_up", 1024, 8192), ("down", 4096, 1024)):
+        g = torch.Generator(device="cuda").manual_seed(K * 7 + N)
+        w0 = (torch.randn((K, N), device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
+        ncopy = max(8, int(pool_bytes // (K * N * 2)) + 1)
+        pool = [w0.clone() for _ in range(ncopy)]
+        a = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+        c = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
+        for i in range(ncopy):
+            torch.matmul(a, pool[i], out=c)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(reps):
+                torch.matmul(a, pool[i % ncopy], out=c)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[f"{name}_{M}x{K}x{N}"] = dict(us=round(us, 3), weight_gbs=round(K * N * 2 / (us * 1e-6) / 1e9, 1))
+        del pool, graph
+        torch.cuda.empty_cache()
+    return out
+
+
+CHAIN_TRACE_PROFILE = os.path.join(ROOT, "profiles", "chain_bf16_m50_launch_gaps.md")
+CHAIN_SOURCES = [os.path.join(ROOT, "gemm_chains_amd", "csrc", f)
+                 for f in ("frt_internal.hpp", "rnq.hip", "gemm.hip", "gemm_kernel.hpp", "gemm_bf16.hip",
+                           "gemm_bf16_silu.hip", "attn.hip", "chain.hip")]
+
+
+def analyze_chain_trace(csv_path, per_decision=None, stall_us=10.0):
+    """Launch gaps of the chain's decisions from a rocprofv3 kernel-trace CSV.
+
+    A decision is a run of consecutive dispatches that starts with the chain's first
+    producer (the producer that reads no partials) and holds per_decision dispatches
+    (7 per layer-step plus the final producer when None: read from the run lengths).  Per
+    decision: span = last end - first start; kernel sum = sum of durations; raw gap share =
+    (span - kernel sum) / span; the same with every gap longer than stall_us left out.
+    Returns the medians over the decisions and the per-decision rows."""
+    import csv
+    import statistics as st
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    ks = [(r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    starts = [i for i, k in enumerate(ks) if "rnq_kernel<0," in k[0]]
+    if per_decision is None:
+        lens = [b - a for a, b in zip(starts, starts[1:])]
+        per_decision = st.mode(lens) if lens else len(ks) - starts[0]
+    dec = []
+    for i in starts:
+        seg = ks[i:i + per_decision]
+        if len(seg) < per_decision:
+            continue
+        span = (seg[-1][2] - seg[0][1]) / 1e3
+        ksum = sum(e - s for _, s, e in seg) / 1e3
+        gaps = [(seg[j + 1][1] - seg[j][2]) / 1e3 for j in range(len(seg) - 1)]
+        big = [g for g in gaps if g > stall_us]
+        dec.append(dict(span_us=round(span, 1), kernel_sum_us=round(ksum, 1),
+                        raw_gap_share=round((span - ksum) / span, 4),
+                        gaps_over_stall=len(big),
+                        gap_share_without_stalls=round((span - sum(big) - ksum) / (span - sum(big)), 4),
+                        median_gap_us=round(st.median(gaps), 3)))
+    med = {k: round(st.median(d[k] for d in dec), 4) for k in dec[0]} if dec else {}
+    return dict(decisions=len(dec), dispatches_per_decision=per_decision, median=med, per_decision=dec)
+
+
+def measured_launch_gaps():
+    """The chain's traced launch-gap shares from the committed summary, or None when the
+    chain's kernel or scheduling code changed since that trace (hash recorded there)."""
+    try:
+        text = open(CHAIN_TRACE_PROFILE, encoding="utf-8").read()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines()
+                  if l.startswith(("source_sha256:", "raw_gap_share:", "gap_share_without_stalls:",
+                                   "gaps_over_10us_per_decision:")))
+    if fields.get("source_sha256", "").strip() != source_hash(CHAIN_SOURCES):
+        return None
+    return {k: float(v.strip()) for k, v in fields.items() if k != "source_sha256"}
 
 
 def cpu_baseline(synth, dims_full, budget_s=12.0, single_budget_s=6.0):
@@ -452,10 +579,18 @@ def main():
     ap.add_argument("--workloads", action="store_true",
                     help="time only the stand-alone workloads (fused RMSNorm + GEMM, gated MLP, FP8 block) "
                          "with cold weights and print them as one JSON line")
+    ap.add_argument("--analyze-trace", metavar="CSV",
+                    help="print the launch-gap shares of the chain's decisions in a rocprofv3 kernel-trace CSV "
+                         "(of a --chain-only run) as JSON, and exit (no GPU needed)")
     ap.add_argument("--chain-only", action="store_true",
                     help="run only the M=50 bf16 chain (read-ahead on) for --warmup + --steps decisions "
                          "(the program the launch-gap kernel trace profiles)")
     args = ap.parse_args()
+    if args.analyze_trace:
+        res = analyze_chain_trace(args.analyze_trace)
+        res["source_sha256"] = source_hash(CHAIN_SOURCES)
+        print(json.dumps(res), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the single-batch action-decoder chain is a "
               "one-device latency path (see the design notes on sharding); use --gpus 1", file=sys.stderr)
@@ -568,6 +703,13 @@ def main():
         f"{us:.2f} us, {achieved:.0f} GB/s")
 
     sweep = gemm_sweep(torch, frt, device, synth)
+    log("stand-alone workloads (configs 1-3)")
+    workloads = stand_alone_workloads(torch, frt, device, synth)
+    log(f"workloads: {workloads}")
+    launch = launch_cost(torch, frt)
+    log(f"dependent launch cost (us per empty kernel in a graph): {launch}")
+    libctx = library_gemm_context(torch)
+    log(f"torch.matmul bf16 at the chain's shapes: {libctx}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -624,6 +766,10 @@ def main():
         "mfma_util_dominant": round(2.0 * dims50["M"] * dims50["hidden"] * 2 * dims50["mlp"] / (us * 1e-6)
                                     / (MFMA_PEAK_TFLOPS["bf16"] * 1e12), 5),
         "gemm_sweep_k2048_n16384": sweep,
+        "workloads": workloads,
+        "launch_cost_us": launch,
+        "launch_gaps_traced": measured_launch_gaps(),
+        "library_gemm_bf16_torch_matmul": libctx,
         "state_reuse_m50_bf16": reuse,
         "cold_weights_m50_bf16": cold,
         "cpu_baseline": cpu,

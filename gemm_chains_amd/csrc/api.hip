@@ -26,3 +26,20 @@ extern "C" const char* frt_status_string(int status) {
 extern "C" int frt_last_hip_error(void) { return frt::g_last_hip_error; }
 
 extern "C" int frt_version(void) { return 100; }
+
+// An empty kernel: what a dependent launch costs before any work.  Each workgroup writes
+// nothing; one lane of workgroup 0 stores its id to `sink` only when `flag` is set (never
+// by the diagnostic below), so the compiler keeps the kernel's body and dispatch.
+__global__ void empty_kernel(unsigned* sink, int flag) {
+  if (flag && blockIdx.x == 0 && threadIdx.x == 0) sink[0] = blockIdx.x;
+}
+
+extern "C" int frt_diag_empty_kernels(void* stream, int n, int workgroups) {
+  FRT_CHECK(n >= 0 && n <= 100000, FRT_E_ARG);
+  FRT_CHECK(workgroups >= 1 && workgroups <= 65536, FRT_E_ARG);
+  for (int i = 0; i < n; ++i) {
+    hipLaunchKernelGGL(empty_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, (unsigned*)nullptr, 0);
+  }
+  FRT_HIP(hipGetLastError());
+  return FRT_OK;
+}
