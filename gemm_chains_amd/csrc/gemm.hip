@@ -17,6 +17,8 @@
 // in wave order, so every result is bitwise deterministic.
 #include "gemm_kernel.hpp"
 
+#include <mutex>
+
 namespace frt {
 
 // Consumer: fixed-order split-K reduction + scale recovery + epilogue.  One thread per
@@ -251,11 +253,13 @@ extern "C" int frt_splitk_choose(int M, int N, int K, int ab_dtype) {
   return choose_splits(M, N, K, ab_dtype, FRT_EPI_NONE);
 }
 
-extern "C" int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int splits, int ab_dtype,
-                                      int layout, const void* a_packed_dev, const void* w_packed_dev,
-                                      const float* w_colscale_dev, float act_scale, float* partials_dev,
-                                      size_t partials_bytes, int epi, void* out_dev, int out_dtype,
-                                      float out_act_scale) {
+// Argument checks of the skinny GEMM entry points (no HIP call).  `splits` is resolved in
+// place (0 = the library's choice).  With scratch_partials the partial sums go to the
+// library's own scratch array, so the caller's partials arguments are not checked.
+static int gemm_validate(int M, int N, int K, int& splits, int ab_dtype, int layout, const void* a_packed_dev,
+                         const void* w_packed_dev, const float* w_colscale_dev, float act_scale,
+                         const float* partials_dev, size_t partials_bytes, bool scratch_partials, int epi,
+                         const void* out_dev, int out_dtype, float out_act_scale) {
   FRT_CHECK(a_packed_dev && w_packed_dev, FRT_E_NULL);
   FRT_CHECK(is_w_dtype(ab_dtype), FRT_E_DTYPE);
   FRT_CHECK(M >= 1 && M <= kMaxM, FRT_E_SHAPE);
@@ -269,37 +273,42 @@ extern "C" int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int spl
   FRT_CHECK(is_split(splits), FRT_E_SPLITK);
   const int ksteps = K / kstep_of(ab_dtype);
   FRT_CHECK(ksteps % splits == 0, FRT_E_SPLITK);
-  FRT_CHECK(epi >= FRT_EPI_NONE && epi <= FRT_EPI_SILU_GATE_QUANT, FRT_E_ARG);
   if (epi == FRT_EPI_SILU_GATE_QUANT) FRT_CHECK(layout == FRT_W_GATE_UP || splits > 1, FRT_E_ARG);
   int st = validate_epilogue_out(M, N, epi, out_dev, out_dtype, out_act_scale);
   if (st != FRT_OK) return st;
-  const void* ptrs[] = {a_packed_dev, w_packed_dev, w_colscale_dev, partials_dev};
+  const void* ptrs[] = {a_packed_dev, w_packed_dev, w_colscale_dev, scratch_partials ? nullptr : partials_dev};
   for (const void* q : ptrs) FRT_CHECK(aligned16(q), FRT_E_ALIGN);
   const bool need_partials = epi == FRT_EPI_NONE || splits > 1;
   const size_t pbytes = (size_t)splits * M * N * 4;
-  if (need_partials) {
+  if (need_partials && !scratch_partials) {
     FRT_CHECK(partials_dev, FRT_E_NULL);
     FRT_CHECK(partials_bytes >= pbytes, FRT_E_WORKSPACE);
   }
   const size_t ab = frt_operand_bytes(act_dtype_of(ab_dtype), M, K);
   const size_t wb = frt_weight_bytes(ab_dtype, K, N);
   const size_t ob = epilogue_out_bytes(M, N, epi, out_dtype);
-  if (need_partials) {
+  if (need_partials && !scratch_partials) {
     FRT_CHECK(!overlaps(partials_dev, pbytes, a_packed_dev, ab), FRT_E_ALIAS);
     FRT_CHECK(!overlaps(partials_dev, pbytes, w_packed_dev, wb), FRT_E_ALIAS);
     FRT_CHECK(!overlaps(partials_dev, pbytes, out_dev, ob), FRT_E_ALIAS);
   }
   FRT_CHECK(!overlaps(out_dev, ob, a_packed_dev, ab), FRT_E_ALIAS);
   FRT_CHECK(!overlaps(out_dev, ob, w_packed_dev, wb), FRT_E_ALIAS);
+  return FRT_OK;
+}
 
+// The GEMM (and, when split with an epilogue, its consumer) on validated arguments.
+static int gemm_enqueue(hipStream_t s, int M, int N, int K, int splits, int ab_dtype, int layout,
+                        const void* a_packed_dev, const void* w_packed_dev, const float* w_colscale_dev,
+                        float act_scale, float* partials_dev, int epi, void* out_dev, int out_dtype,
+                        float out_act_scale) {
   GemmParams p{};
   p.M = M; p.N = N; p.K = K; p.MB = m_blocks(M); p.splits = splits;
-  p.ab_dtype = ab_dtype; p.layout = layout; p.ksteps_per_split = ksteps / splits;
+  p.ab_dtype = ab_dtype; p.layout = layout; p.ksteps_per_split = K / kstep_of(ab_dtype) / splits;
   p.a = (const uint8_t*)a_packed_dev; p.w = (const uint8_t*)w_packed_dev; p.colscale = w_colscale_dev;
   p.act_scale = act_scale; p.act_scale_ptr = nullptr; p.partials = partials_dev;
   p.epi = epi; p.out = out_dev; p.out_dtype = out_dtype; p.out_scale = out_dtype == FRT_E4M3 ? out_act_scale : 1.f;
   p.out_scale_ptr = nullptr;
-  hipStream_t s = (hipStream_t)stream;
   FRT_HIP(launch_gemm(p, s));
   if (splits > 1 && epi != FRT_EPI_NONE) {
     ReduceParams r{};
@@ -309,6 +318,70 @@ extern "C" int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int spl
     FRT_HIP(launch_reduce(r, s));
   }
   return FRT_OK;
+}
+
+extern "C" int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int splits, int ab_dtype,
+                                      int layout, const void* a_packed_dev, const void* w_packed_dev,
+                                      const float* w_colscale_dev, float act_scale, float* partials_dev,
+                                      size_t partials_bytes, int epi, void* out_dev, int out_dtype,
+                                      float out_act_scale) {
+  const int st = gemm_validate(M, N, K, splits, ab_dtype, layout, a_packed_dev, w_packed_dev, w_colscale_dev,
+                               act_scale, partials_dev, partials_bytes, false, epi, out_dev, out_dtype,
+                               out_act_scale);
+  if (st != FRT_OK) return st;
+  return gemm_enqueue((hipStream_t)stream, M, N, K, splits, ab_dtype, layout, a_packed_dev, w_packed_dev,
+                      w_colscale_dev, act_scale, partials_dev, epi, out_dev, out_dtype, out_act_scale);
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// For callers that cannot allocate device memory (code under graph capture, tight serving
+// loops): the split-K partials of frt_skinny_gemm_splitk_noalloc live in this file-scope
+// array, one copy per GPU, held from the library's load until the process ends.  Host
+// code never uses the array's name as an address: the device address of each GPU's copy
+// comes from hipGetSymbolAddress, once per device (on the first call made with that
+// device current), and is kept per device.  Every call on a GPU shares its copy, so calls
+// that overlap in time on one GPU race; the partials are fully rewritten by every call
+// that uses them (nothing needs clearing).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices] = {};
+
+static int scratch_of_current_device(float** out) {
+  int dev = -1;
+  FRT_HIP(hipGetDevice(&dev));
+  FRT_CHECK(dev >= 0 && dev < kMaxDevices, FRT_E_STATE);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    FRT_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    FRT_CHECK(p != nullptr, FRT_E_HIP);
+    g_scratch_dev[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_dev[dev]);
+  return FRT_OK;
+}
+
+extern "C" size_t frt_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int frt_skinny_gemm_splitk_noalloc(void* stream, int M, int N, int K, int splits, int ab_dtype,
+                                              int layout, const void* a_packed_dev, const void* w_packed_dev,
+                                              const float* w_colscale_dev, float act_scale, int epi,
+                                              void* out_dev, int out_dtype, float out_act_scale) {
+  FRT_CHECK(epi == FRT_EPI_STORE_F32 || epi == FRT_EPI_STORE_BF16 || epi == FRT_EPI_SILU_GATE_QUANT, FRT_E_ARG);
+  int st = gemm_validate(M, N, K, splits, ab_dtype, layout, a_packed_dev, w_packed_dev, w_colscale_dev, act_scale,
+                         nullptr, 0, true, epi, out_dev, out_dtype, out_act_scale);
+  if (st != FRT_OK) return st;
+  FRT_CHECK((size_t)splits * M * N * 4 <= kScratchBytes, FRT_E_WORKSPACE);
+  float* partials = nullptr;
+  if (splits > 1) {
+    st = scratch_of_current_device(&partials);
+    if (st != FRT_OK) return st;
+  }
+  return gemm_enqueue((hipStream_t)stream, M, N, K, splits, ab_dtype, layout, a_packed_dev, w_packed_dev,
+                      w_colscale_dev, act_scale, partials, epi, out_dev, out_dtype, out_act_scale);
 }
 
 extern "C" int frt_splitk_reduce(void* stream, int M, int N, int splits, const float* partials_dev,

@@ -68,6 +68,9 @@ _SIGS = {
                                        _c_void_p]),
     "frt_skinny_gemm_splitk": (_int, [_c_void_p, _int, _int, _int, _int, _int, _int, _c_void_p, _c_void_p,
                                       _c_void_p, _float, _c_void_p, _size, _int, _c_void_p, _int, _float]),
+    "frt_skinny_gemm_splitk_noalloc": (_int, [_c_void_p, _int, _int, _int, _int, _int, _int, _c_void_p, _c_void_p,
+                                              _c_void_p, _float, _int, _c_void_p, _int, _float]),
+    "frt_noalloc_scratch_bytes": (_size, []),
     "frt_splitk_reduce": (_int, [_c_void_p, _int, _int, _int, _c_void_p, _float, _c_void_p, _int, _c_void_p,
                                  _int, _float]),
     "frt_splitk_choose": (_int, [_int, _int, _int, _int]),
@@ -237,6 +240,17 @@ def frt_skinny_gemm_splitk(M, N, K, splits, ab_dtype, layout, a_packed, w_packed
                                          _ptr(w_packed), _ptr(w_colscale), act_scale, _ptr(partials),
                                          partials_bytes, epi, _ptr(out), out_dtype, out_act_scale),
            "frt_skinny_gemm_splitk")
+
+
+def frt_skinny_gemm_splitk_noalloc(M, N, K, splits, ab_dtype, layout, a_packed, w_packed, w_colscale, act_scale, epi,
+                                   out, out_dtype, out_act_scale, stream=None):
+    _check(_lib().frt_skinny_gemm_splitk_noalloc(_stream(stream), M, N, K, splits, ab_dtype, layout, _ptr(a_packed),
+                                                 _ptr(w_packed), _ptr(w_colscale), act_scale, epi, _ptr(out),
+                                                 out_dtype, out_act_scale), "frt_skinny_gemm_splitk_noalloc")
+
+
+def frt_noalloc_scratch_bytes():
+    return _lib().frt_noalloc_scratch_bytes()
 
 
 def frt_splitk_reduce(M, N, splits, partials, act_scale, w_colscale, epi, out, out_dtype, out_act_scale,

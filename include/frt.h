@@ -182,6 +182,25 @@ int frt_skinny_gemm_splitk(void* stream, int M, int N, int K, int splits,
                            float act_scale, float* partials_dev, size_t partials_bytes,
                            int epi, void* out_dev, int out_dtype, float out_act_scale);
 
+/* Allocation-free variant of frt_skinny_gemm_splitk, for callers that cannot allocate
+ * device memory (code under hipGraph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as frt_skinny_gemm_splitk with an epilogue
+ * (epi STORE_F32, STORE_BF16 or SILU_GATE_QUANT; FRT_E_ARG for FRT_EPI_NONE, whose
+ * partials are the caller's output), minus the partials workspace: when splits resolves
+ * to more than 1, the [splits][M][N] fp32 partials go to a scratch array inside the
+ * library, one per GPU, of frt_noalloc_scratch_bytes() bytes (16 MiB), held from the first
+ * call on that GPU until the process ends.  splits * M * N * 4 above that size returns
+ * FRT_E_WORKSPACE before anything is enqueued.  The call allocates nothing.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap in time on one GPU (different
+ * streams, different threads) race and must be ordered by the caller; each call fully
+ * rewrites the partials it reads.                                                       */
+int frt_skinny_gemm_splitk_noalloc(void* stream, int M, int N, int K, int splits,
+                                   int ab_dtype, int layout, const void* a_packed_dev,
+                                   const void* w_packed_dev, const float* w_colscale_dev,
+                                   float act_scale, int epi, void* out_dev, int out_dtype,
+                                   float out_act_scale);
+size_t frt_noalloc_scratch_bytes(void);
+
 /* Split-K consumer on its own: reduce [splits][M][N] partials (ascending j), recover
  * scales, then apply `epi` (STORE_F32, STORE_BF16 or SILU_GATE_QUANT; for the latter
  * the columns are in logical order, gate = [0, N/2)).                                */
