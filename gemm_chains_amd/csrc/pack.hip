@@ -12,20 +12,41 @@
 
 namespace frt {
 
-// s_w[n] = max_k |gamma[k] * W[k][n]| / 448, one thread per column; consecutive threads
-// read consecutive columns of a row, so every row read is coalesced.  The products are
-// exact in float64 (8 x 24 significand bits) and the quotient is rounded once to fp32.
-__global__ void __launch_bounds__(256) colscale_kernel(const uint16_t* __restrict__ w, const float* __restrict__ gamma,
-                                                       int K, int N, float* __restrict__ colscale) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
+// s_w[n] = max_k |gamma[k] * W[k][n]| / 448.  Workgroup = 64 consecutive columns (one per
+// lane, so every row a wave reads is 128 contiguous bytes); its 16 waves take interleaved
+// runs of 16 rows with all 16 loads in flight before the first is used, and the waves'
+// maxima meet in LDS.  The products are exact in float64 (8 x 24 significand bits), a
+// maximum does not depend on the order it is taken in, and the quotient is rounded once to
+// fp32.  (One thread per column walking all of K left 16 waves on the whole chip for a
+// 1024-column weight: 740 us per call on MI355X.)
+constexpr int kColscaleWaves = 16, kColscaleRows = 16;
+__global__ void __launch_bounds__(64 * kColscaleWaves) colscale_kernel(const uint16_t* __restrict__ w,
+                                                                       const float* __restrict__ gamma, int K, int N,
+                                                                       float* __restrict__ colscale) {
+  __shared__ double part[kColscaleWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = blockIdx.x * 64 + lane;
+  const int nn = n < N ? n : N - 1;  // lanes past the last column read an in-bounds stand-in
   double amax = 0.0;
-  for (int k = 0; k < K; ++k) {
-    double v = (double)bf16_to_f32(w[(size_t)k * N + n]);
-    if (gamma) v *= (double)gamma[k];
-    amax = fmax(amax, fabs(v));
+  for (int k0 = wave * kColscaleRows; k0 < K; k0 += kColscaleWaves * kColscaleRows) {
+    double v[kColscaleRows];
+#pragma unroll
+    for (int e = 0; e < kColscaleRows; ++e) {
+      const int k = k0 + e < K ? k0 + e : K - 1;
+      v[e] = (double)bf16_to_f32(w[(size_t)k * N + nn]);
+      if (gamma) v[e] *= (double)gamma[k];
+    }
+#pragma unroll
+    for (int e = 0; e < kColscaleRows; ++e) amax = fmax(amax, fabs(v[e]));  // a repeated row changes no maximum
   }
-  colscale[n] = (float)(amax / 448.0);
+  part[wave][lane] = amax;
+  __syncthreads();
+  if (wave == 0 && n < N) {
+    double m = part[0][lane];
+#pragma unroll
+    for (int i = 1; i < kColscaleWaves; ++i) m = fmax(m, part[i][lane]);
+    colscale[n] = (float)(m / 448.0);
+  }
 }
 
 // One thread per 16-byte lane slot of the packed weight.
@@ -274,7 +295,8 @@ extern "C" int frt_pack_weight(void* stream, int K, int N, const uint16_t* w_bf1
     return FRT_OK;
   }
   if (dtype == FRT_E4M3) {
-    hipLaunchKernelGGL(colscale_kernel, dim3((N + 255) / 256), dim3(256), 0, s, w_bf16_dev, gamma_dev, K, N, colscale_dev);
+    hipLaunchKernelGGL(colscale_kernel, dim3((N + 63) / 64), dim3(64 * kColscaleWaves), 0, s, w_bf16_dev, gamma_dev,
+                       K, N, colscale_dev);
     FRT_HIP(hipGetLastError());
   }
   const size_t nslots = pb / 16;

@@ -30,3 +30,17 @@ def canaries(monkeypatch):
     monkeypatch.setattr(device, "empty_f32", cz.f32)
     yield cz
     cz.check()
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Print the parity figures the tests recorded (end-to-end errors, teacher-forced worst
+    cases, converter counts), also under -q."""
+    try:
+        from tests.helpers import FIGURES
+    except Exception:
+        return
+    if not FIGURES:
+        return
+    terminalreporter.write_sep("-", "parity figures")
+    for label in sorted(FIGURES):
+        terminalreporter.write_line(f"{label}: {FIGURES[label]}")

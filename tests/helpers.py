@@ -106,3 +106,12 @@ class Canaries:
             assert np.all(head == self.BYTE), f"buffer {i} ({n} bytes): canary before it overwritten"
             assert np.all(tail == self.BYTE), f"buffer {i} ({n} bytes): canary after it overwritten"
         return len(self.bufs)
+
+
+# Parity figures measured during the session, printed in pytest's terminal summary (so a
+# quiet run still reports them): label -> text.
+FIGURES = {}
+
+
+def record(label, text):
+    FIGURES[label] = text

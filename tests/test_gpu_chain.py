@@ -33,7 +33,7 @@ import torch
 import synth
 from oracle import codec, ref
 from tests import chain_parity as cp
-from tests.helpers import rel_l2
+from tests.helpers import record, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,11 @@ def _oracle_and_bar(wl, ws, scales, adt, seeds=(95, 96, 97)):
     return want, sens, 2.0 * max(sens, 1e-7)
 
 
+def _figs(worst, err, sens):
+    return (f"teacher-forced residual {worst['h']:.1e}, partials {max(worst['p_o'], worst['p_down']):.1e}, "
+            f"codes off {100 * worst['code_frac']:.2f} %; end to end {err:.3e} (oracle sensitivity {sens:.3e})")
+
+
 def _run(chain, dims, packed, wl, scales, **kw):
     ch = chain.Chain(dims, packed, **kw)
     chain.load_workload(ch, wl, scales)
@@ -106,6 +111,7 @@ def test_chain_parity(F, wdtype, M, splits):
     err = rel_l2(got, want)
     log(f"chain {wdtype} M={M} splits={splits}: teacher-forced worst {worst}; end to end rel L2 {err:.3e}, "
         f"oracle sensitivity {sens:.3e}, bar {bar:.3e}, kernels {cg.kernel_count()}")
+    record(f"chain 2x2 {wdtype} M={M} splits={splits}", _figs(worst, err, sens))
     assert err <= bar
     # replay twice: bit-identical; eager launches of the production chain: bit-identical
     cg.run()
@@ -144,6 +150,7 @@ def test_chain_edge_shapes(F, M, prefix):
     err = rel_l2(got, want)
     log(f"chain M={M} prefix={prefix}: teacher-forced worst {worst}; end to end rel L2 {err:.3e}, "
         f"oracle sensitivity {sens:.3e}")
+    record(f"chain 2x2 bf16 M={M} prefix={prefix}", _figs(worst, err, sens))
     assert err <= bar
     assert np.array_equal(d["x_out"], got), "production (fused, read-ahead) vs debug chain"
 
@@ -200,6 +207,7 @@ def test_full_decision_parity(F, wdtype, M):
     t = time.time()
     worst = cp.teacher_forced_check(d, wl["x0"], wl["mod"], kp, vp, ws, scales, dims, adt, steps=[0, 9])
     log(f"full decision {wdtype} M={M}: teacher-forced steps 0 and 9 pass ({time.time() - t:.1f} s), worst {worst}")
+    record(f"decision 18x10 {wdtype} M={M}", _figs(worst, err, sens))
     assert err <= bar
 
 
@@ -243,5 +251,6 @@ def test_chain_calibration_matches_oracle(F):
     want = ref.calibrate(wl["x0"], cp.oracle_weights(wl["layers"], "bf16"), kp, vp, wl["mod"], dims, 1e-6)
     rel = np.abs(got - want) / want
     log(f"calibration scales rel diff: max {rel.max():.2e}, per site {rel.round(5).tolist()}")
+    record("GPU calibration vs oracle (max rel diff of the scales)", f"{rel.max():.2e}")
     assert rel.max() <= 0.02
     assert np.all(np.isfinite(x_cal))

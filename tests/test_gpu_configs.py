@@ -31,7 +31,7 @@ import torch
 
 import synth
 from oracle import codec, ref
-from tests.helpers import check_codes, rel_l2, silu_gate_mag
+from tests.helpers import check_codes, record, rel_l2, silu_gate_mag
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("canaries")]
 
@@ -121,6 +121,8 @@ def test_config1_fused_rmsnorm_bf16_gemm(F):
         assert rel_l2(bf, c_emul) <= 5e-3, f"s={s} bf16 output"
         print(f"config 1 s={s}: rel L2 vs emulating {rel_l2(outs[s], c_emul):.2e}, vs plain "
               f"{rel_l2(outs[s], c_plain):.2e}")
+        record(f"config 1 bf16 s={s}", f"C vs emulating {rel_l2(outs[s], c_emul):.2e} (bar 5e-3), "
+                                       f"vs plain definition {rel_l2(outs[s], c_plain):.2e}")
     for s in (2, 4):
         assert rel_l2(outs[s], outs[1]) <= 1e-5, f"split {s} vs unsplit"
 
@@ -154,6 +156,7 @@ def test_config2_gated_mlp_bf16(F):
         e2e = rel_l2(codec.bf16_decode(zc[:M]), z["deq"])
         assert e2e <= 5e-3, f"config 2 SiLU s={s} end to end"
         print(f"config 2 up s={s}: SiLU output rel L2 end to end {e2e:.2e}")
+        record(f"config 2 bf16 gate|up s={s}", f"SiLU output end to end {e2e:.2e} (bar 5e-3)")
     downs = {}
     for s in (1, 2, 4, 8):
         c = _gemm_f32(frt, dev, M, K, Fm, s, frt.BF16, frt.W_PLAIN, zs[1], wd, None, 1.0)
@@ -161,6 +164,7 @@ def test_config2_gated_mlp_bf16(F):
         downs[s] = dev.to_np(c)
         assert rel_l2(downs[s], c_down) <= 5e-3, f"down s={s}"
         print(f"config 2 down s={s}: rel L2 {rel_l2(downs[s], c_down):.2e}")
+        record(f"config 2 bf16 down s={s}", f"C end to end {rel_l2(downs[s], c_down):.2e} (bar 5e-3)")
     for s in (2, 4, 8):
         assert rel_l2(downs[s], downs[1]) <= 1e-5, f"down split {s} vs unsplit"
     # teacher-forced down projection: the oracle's SiLU codes, host-packed
@@ -236,6 +240,9 @@ def test_config3_fp8_static_scale_block(F):
     # sensitivity reading (twice the oracle's own change), and the print says which.
     print(f"config 3 end to end vs the stated 2e-3: SiLU {'meets' if e2e_z <= 2e-3 else 'MISSES'}, "
           f"down {'meets' if e2e <= 2e-3 else 'MISSES'}")
+    record("config 3 fp8 end to end", f"SiLU {e2e_z:.2e}, down {e2e:.2e} against the stated 2e-3 "
+                                      f"({'met' if max(e2e_z, e2e) <= 2e-3 else 'MISSED'}; passes under 2 x oracle "
+                                      f"sensitivity {sens_z:.2e} / {sens_d:.2e})")
     assert e2e_z <= 2 * sens_z, "config 3 SiLU end to end"
     assert e2e <= 2 * sens_d, "config 3 down end to end"
     # teacher-forced down projection
@@ -285,3 +292,4 @@ def test_config5_gate_up_sweep(F, M, dtype):
     _silu_teacher_forced(frt, dev, M, N, K, 1, dt, dtype, o, wp, cs, codec.decode(wc, dtype), ws, s_y, s_z,
                          f"config 5 SiLU M={M} {dtype}")
     print(f"config 5 M={M} {dtype}: split {s_tab}, C rel L2 {rel_l2(got, c):.2e}, SiLU output rel L2 {e2e:.2e}")
+    record(f"config 5 {dtype} M={M}", f"C {rel_l2(got, c):.2e}, SiLU output end to end {e2e:.2e}")

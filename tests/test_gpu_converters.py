@@ -30,6 +30,7 @@ import pytest
 import torch
 
 from oracle import codec
+from tests.helpers import record
 
 pytestmark = pytest.mark.gpu
 
@@ -136,6 +137,7 @@ def test_converter_edges(F, dtype):
     got = _convert(frt, device, bits, frt.DTYPES[dtype])
     _compare(got, bits, dtype)
     print(f"{dtype} converter: {bits.size} edge values bit-exact", flush=True)
+    record(f"converter {dtype} edges", f"{bits.size} values bit-exact")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
@@ -146,3 +148,4 @@ def test_converter_random(F, dtype):
     got = _convert(frt, device, bits, frt.DTYPES[dtype])
     _compare(got, bits, dtype)
     print(f"{dtype} converter: {bits.size} random values bit-exact", flush=True)
+    record(f"converter {dtype} random", f"{bits.size} values bit-exact")
