@@ -127,30 +127,34 @@ def test_chain_parity(F, wdtype, M, splits):
     ce.close()
 
 
-@pytest.mark.parametrize("M,prefix", [(1, 0), (64, 100), (17, 300), (50, 0)])
-def test_chain_edge_shapes(F, M, prefix):
+@pytest.mark.parametrize("M,prefix,wdtype", [(1, 0, "bf16"), (64, 100, "bf16"), (17, 300, "bf16"), (50, 0, "bf16"),
+                                             (1, 0, "e4m3"), (64, 100, "mxfp4"), (17, 300, "e4m3"), (33, 31, "mxfp4")])
+def test_chain_edge_shapes(F, M, prefix, wdtype):
     """Smallest and largest action chunks and short prefixes: no prefix (one key chunk,
     the merge kernel not needed), and prefixes that give 2..4 chunks (merge fused into
-    the O projection).  bf16; teacher-forced and end to end against the oracle; the
-    production chain (fused, read-ahead on) must equal the debug chain bit for bit."""
+    the O projection), in bf16, e4m3 and MXFP4 weights; teacher-forced and end to end
+    against the oracle; the production chain (fused, read-ahead on) must equal the debug
+    chain bit for bit."""
     frt, chain = F
     dims = synth.chain_dims(layers=2, steps=2, M=M, prefix=prefix)
     wl = synth.workload4(dims)
-    ws = cp.oracle_weights(wl["layers"], "bf16")
-    want, sens, bar = _oracle_and_bar(wl, ws, None, "bf16")
+    ws = cp.oracle_weights(wl["layers"], wdtype)
+    adt = "bf16" if wdtype == "bf16" else "e4m3"
+    scales = _oracle_scales(wl, dims) if adt == "e4m3" else None
+    want, sens, bar = _oracle_and_bar(wl, ws, scales, adt)
     kp, vp = _prefixes(wl)
-    packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
-    cd = _run(chain, dims, packed, wl, None, use_graph=True, keep_intermediates=True)
-    d = cp.gpu_dumps(frt, cd, dims, frt.BF16)
-    worst = cp.teacher_forced_check(d, wl["x0"], wl["mod"], kp, vp, ws, None, dims, "bf16")
+    packed = chain.PackedLayers(wl["layers"], dims, frt.DTYPES[wdtype])
+    cd = _run(chain, dims, packed, wl, scales, use_graph=True, keep_intermediates=True)
+    d = cp.gpu_dumps(frt, cd, dims, frt.DTYPES[wdtype])
+    worst = cp.teacher_forced_check(d, wl["x0"], wl["mod"], kp, vp, ws, scales, dims, adt)
     cd.close()
-    cpf = _run(chain, dims, packed, wl, None, use_graph=True, prefetch_next=True)
+    cpf = _run(chain, dims, packed, wl, scales, use_graph=True, prefetch_next=True)
     got = cpf.read("x_out").reshape(M, -1)
     cpf.close()
     err = rel_l2(got, want)
-    log(f"chain M={M} prefix={prefix}: teacher-forced worst {worst}; end to end rel L2 {err:.3e}, "
+    log(f"chain {wdtype} M={M} prefix={prefix}: teacher-forced worst {worst}; end to end rel L2 {err:.3e}, "
         f"oracle sensitivity {sens:.3e}")
-    record(f"chain 2x2 bf16 M={M} prefix={prefix}", _figs(worst, err, sens))
+    record(f"chain 2x2 {wdtype} M={M} prefix={prefix}", _figs(worst, err, sens))
     assert err <= bar
     assert np.array_equal(d["x_out"], got), "production (fused, read-ahead) vs debug chain"
 
