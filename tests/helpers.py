@@ -8,12 +8,21 @@ when it lies (in value order) between encode(v - TAU*mag) and encode(v + TAU*mag
 the size of the summands that produced v, so cancellation cannot shrink the band below
 float32's own error.  TAU = 2**-17 is 128 float32 ulps of the summands.  Rounding is
 monotone, so the interval test is exact.
+
+Count limit: at most max_frac of the codes may differ, which catches a drift that stays
+inside the band.  A differing code whose oracle value sits within FP32_TIE (relative to
+the value itself) of the midpoint between the two codes is a tie that float32 cannot
+decide the way float64 does (its own rounding of the scale alone is 2**-24); such codes
+are not counted.  They are common only where the inputs are themselves coarse, e.g. a
+single key, whose attention output is a bf16 value of V, over a scale that is a bf16
+maximum / 448.
 """
 import numpy as np
 
 from oracle import codec
 
 TAU = 2.0 ** -17
+FP32_TIE = 2.0 ** -21
 
 
 def _ordinal(codes, dtype):
@@ -33,6 +42,7 @@ def check_codes(gpu_codes, v, mag, dtype, tau=TAU, max_frac=0.01, label=""):
     want = codec.encode(v, dtype)
     assert gpu_codes.shape == want.shape, (gpu_codes.shape, want.shape)
     diff = np.flatnonzero(gpu_codes.ravel() != want.ravel())
+    n_ties = 0
     if len(diff):
         vv = v.ravel()[diff]
         band = tau * mag.ravel()[diff]
@@ -47,7 +57,12 @@ def check_codes(gpu_codes, v, mag, dtype, tau=TAU, max_frac=0.01, label=""):
                 f"{label}: {len(bad)} codes outside the tie band of {len(diff)} differing "
                 f"(of {v.size}); first at flat index {i}: gpu {int(gpu_codes.ravel()[i]):#x} "
                 f"oracle {int(want.ravel()[i]):#x} value {v.ravel()[i]!r} mag {mag.ravel()[i]!r}")
-    assert len(diff) <= max_frac * v.size, f"{label}: {len(diff)} of {v.size} codes differ"
+        w = want.ravel()[diff]
+        mid = 0.5 * (codec.decode(gpu_codes.ravel()[diff], dtype) + codec.decode(w, dtype))
+        adjacent = np.abs(g - _ordinal(w, dtype)) == 1
+        n_ties = int(np.count_nonzero(adjacent & (np.abs(vv - mid) <= FP32_TIE * np.abs(vv))))
+    assert len(diff) - n_ties <= max_frac * v.size, (
+        f"{label}: {len(diff)} of {v.size} codes differ ({n_ties} of them at a float32 tie)")
     return len(diff), v.size
 
 
