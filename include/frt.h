@@ -34,7 +34,8 @@
  *     exception crosses the ABI.
  *   - Shapes: 1 <= M <= 64 action rows.  bf16 operands need K % 32 == 0, e4m3 operands
  *     K % 128 == 0; N % 16 == 0.  M is padded to Mp = 16 * ceil(M / 16) in packed
- *     operands; padding rows are written as zero codes by every producer.
+ *     operands; padding rows are written as zero codes by every producer, and no GEMM
+ *     result depends on them.
  *   - Numbers: bf16 = bfloat16, round to nearest even.  e4m3 = OCP E4M3FN, round to
  *     nearest even, saturating to +-448, NaN -> 0x7F.
  */

@@ -255,6 +255,46 @@ def test_gemm_silu_gate_epilogue(F, M, N, K, dtype, splits):
     assert np.all(codes[M:] == 0)
 
 
+@pytest.mark.parametrize("M,N,K,dtype", [(50, 8192, 1024, "bf16"), (10, 1024, 4096, "bf16"), (17, 2560, 1024, "bf16"),
+                                         (50, 1024, 1024, "e4m3")])
+def test_gemm_results_ignore_operand_padding_rows(F, M, N, K, dtype):
+    """The padding rows of a packed operand (rows M .. Mp-1) never reach a stored result:
+    partials and the SiLU-gate output are bitwise the same whether those rows hold zero
+    codes or other finite codes."""
+    frt, dev = F
+    dt = frt.DTYPES[dtype]
+    Mp = 16 * math.ceil(M / 16)
+    w_bits = synth.weight_bf16(5, 93, 1, K, N)
+    wcodes, s_w, _ = ref.pack_weight_values(codec.bf16_decode(w_bits), None, dtype)
+    a_val = synth.normal(5, 93, 2, (Mp, K))
+    full = synth.to_bf16_bits(a_val) if dtype == "bf16" else codec.e4m3_encode(a_val.astype(np.float64) * 60.0)
+    clean = dev.to_dev(frt.frt_operand_pack_host(full[:M], dt, M, K))      # padding rows: zero codes
+    dirty = dev.to_dev(frt.frt_operand_pack_host(full, dt, Mp, K))         # padding rows: finite codes
+    assert not torch.equal(clean, dirty)
+    cs = dev.to_dev(s_w.astype(np.float32)) if dtype == "e4m3" else None
+    act = 0.015625 if dtype == "e4m3" else 1.0
+    out_scale = 0.05 if dtype == "e4m3" else 1.0
+    got = {}
+    for name, a_pk in (("clean", clean), ("dirty", dirty)):
+        for layout, epi in ((frt.W_PLAIN, frt.EPI_NONE), (frt.W_GATE_UP, frt.EPI_SILU_GATE_QUANT)):
+            w_pk = dev.to_dev(frt.frt_weight_pack_host(wcodes, dt, K, N, layout))
+            if epi == frt.EPI_NONE:
+                parts = dev.empty_f32(1, M, N)
+                frt.frt_skinny_gemm_splitk(M, N, K, 1, dt, layout, a_pk, w_pk, None, 1.0, parts, parts.numel() * 4,
+                                           epi, None, dt, 1.0)
+                torch.cuda.synchronize()
+                got[name, epi] = dev.to_np(parts)
+            else:
+                out = dev.empty_bytes(frt.frt_operand_bytes(dt, M, N // 2))
+                out.fill_(0xCD)
+                frt.frt_skinny_gemm_splitk(M, N, K, 1, dt, layout, a_pk, w_pk, cs, act, None, 0, epi, out, dt,
+                                           out_scale)
+                torch.cuda.synchronize()
+                got[name, epi] = out.cpu().numpy()
+    for epi in (frt.EPI_NONE, frt.EPI_SILU_GATE_QUANT):
+        assert np.array_equal(got["clean", epi], got["dirty", epi]), f"epilogue {epi}"
+
+
 # ------------------------------------------------------------------ fused QKV GEMM
 
 @pytest.mark.parametrize("M,K,dtype,splits", [(50, 1024, "bf16", 1), (50, 1024, "bf16", 4), (10, 1024, "e4m3", 1),
