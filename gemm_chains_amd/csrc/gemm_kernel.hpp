@@ -50,6 +50,10 @@ struct Frag<FRT_MXFP4> {
   unsigned s;  // its E8M0 scale byte
 };
 
+// Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, raw (stride 0)
+// addressing; loads at offsets >= the resource's byte count return zeros.
+constexpr int kBufferWord3 = 0x00020000;
+
 // VGPRs a fragment holds per lane (the register budget of a round's loads).
 constexpr int frag_regs(int dt) { return dt == FRT_BF16 ? 4 : (dt == FRT_MXFP4 ? 5 : 8); }
 
@@ -169,23 +173,34 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
   // ks_begin + u.  run = PER * rounds, rounds >= 1.
   Frag<DT> wf[PER][NT];
   Frag<ADT> af[PER][MB];
-  // A partial last 16-row block (M = 50: 2 real rows of 16): with bf16 operands the
-  // lanes of its padding rows load nothing, since their columns of the product are never
-  // stored.  Measured on MI355X (paired, bitwise equal outputs): the M=50 bf16 chain
-  // 29.59 -> 29.10 us/layer, M=10 25.38 -> 25.23, the gate|up GEMM 6.05 -> 5.92 us; the
-  // same masking of e4m3 operands lost 0.13 us/layer at M=50 and is not used.
+  // A partial last 16-row block (M = 50: 2 real rows of 16): the lanes of its padding
+  // rows load nothing, since their columns of the product are never stored.  bf16
+  // operands skip those lanes under EXEC; e4m3 operands read the tile through a buffer
+  // resource that ends at the tile, with padding lanes addressed past it (zeros, no memory
+  // access; an EXEC-masked e4m3 load made the compiler wait for the loads in flight
+  // inside the masked block).  Measured on MI355X (paired, bitwise equal outputs): bf16
+  // chain 29.59 -> 29.15 us/layer at M=50 and 25.38 -> 25.23 at M=10 (the buffer form
+  // gave 29.32 / 25.49 there); e4m3 chain 26.97 -> 26.77 at M=50, 23.94 -> 23.87 at M=10;
+  // MXFP4 weights (e4m3 operands) 25.66 -> 25.53 at M=50.
   const int rem_last = p.M - (mb0 + MB - 1) * 16;  // real rows of the last block (>= 16: full)
-  const bool mask_last = ADT == FRT_BF16 && rem_last < 16;
+  const bool part_last = rem_last < 16;
   const bool lane_row_live = (lane & 15) < rem_last;
+  const int voff = lane_row_live ? lane * 16 : TB;
   auto load_slot = [&](int u, int ks) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) load_frag<DT, true>(wf[u][t], wbase[t] + (size_t)ks * TBW, lane);
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
       const uint8_t* at = abase + (size_t)ks * astep + (size_t)b * TB;
-      if (b == MB - 1 && mask_last) {
-        af[u][b] = Frag<ADT>{};
-        if (lane_row_live) load_frag<ADT, false>(af[u][b], at, lane);
+      if (b == MB - 1 && part_last) {
+        if constexpr (ADT == FRT_BF16) {
+          af[u][b] = Frag<ADT>{};
+          if (lane_row_live) load_frag<ADT, false>(af[u][b], at, lane);
+        } else {
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)at, (short)0, TB, kBufferWord3);
+          af[u][b].v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+          af[u][b].v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 1024, 0, 0);
+        }
       } else {
         load_frag<ADT, false>(af[u][b], at, lane);
       }
