@@ -127,7 +127,7 @@ __device__ __forceinline__ float silu_f(float g) {
 // FAST (GemmFast) fixes four waves and a single round, and with kFastPlain drops the
 // pointer-read scales: measured on MI355X, the shorter, branch-free code saves 0.4 us per
 // launch of the gate|up GEMM.
-template <int DT, int MB, int NT, int PER, int EPI, int FAST>
+template <int DT, int MB, int NT, int PER, int EPI, int FAST, bool PAD>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
   constexpr bool SHAPE = FAST != kGeneric, PLAIN = FAST == kFastPlain;
   constexpr int ADT = act_dtype_of(DT);   // operand (activation) format
@@ -173,17 +173,20 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
   // ks_begin + u.  run = PER * rounds, rounds >= 1.
   Frag<DT> wf[PER][NT];
   Frag<ADT> af[PER][MB];
-  // A partial last 16-row block (M = 50: 2 real rows of 16): the lanes of its padding
-  // rows load nothing, since their columns of the product are never stored.  bf16
-  // operands skip those lanes under EXEC; e4m3 operands read the tile through a buffer
-  // resource that ends at the tile, with padding lanes addressed past it (zeros, no memory
-  // access; an EXEC-masked e4m3 load made the compiler wait for the loads in flight
-  // inside the masked block).  Measured on MI355X (paired, bitwise equal outputs): bf16
-  // chain 29.59 -> 29.15 us/layer at M=50 and 25.38 -> 25.23 at M=10 (the buffer form
-  // gave 29.32 / 25.49 there); e4m3 chain 26.97 -> 26.77 at M=50, 23.94 -> 23.87 at M=10;
-  // MXFP4 weights (e4m3 operands) 25.66 -> 25.53 at M=50.
+  // PAD kernels (M not a multiple of 16, single-round shapes): the lanes of the padding
+  // rows of the last 16-row block (M = 50: 14 of 16) load nothing, since their columns of
+  // the product are never stored.  bf16 operands skip them under EXEC; e4m3 operands read
+  // the tile through a buffer resource that ends at the tile, with those lanes addressed
+  // past its end (zeros, no memory access; an EXEC-masked e4m3 load made the compiler copy
+  // a loaded register inside the masked block and wait there for every load in flight).
+  // Measured on MI355X (paired on one box, bitwise equal outputs): bf16 chain 29.58 ->
+  // 29.11 us/layer at M=50, 26.31 -> 25.37 at M=10; e4m3 26.84 -> 26.66 at M=50; MXFP4
+  // weights 25.63 -> 25.47.  It is a compile-time variant: a run-time test around the
+  // masked loads made kernels wait for more loads before their first MFMA, masked or not
+  // (the K=2048 sweep's two-round bf16 GEMM at M=64: 16.3 -> 17.6 us; e4m3 at M=32: 8.3 ->
+  // 8.6 us), and cost 0.8 us per layer of the M=10 bf16 chain.  bf16 through the buffer
+  // resource instead of EXEC: 29.44 at M=50.
   const int rem_last = p.M - (mb0 + MB - 1) * 16;  // real rows of the last block (>= 16: full)
-  const bool part_last = rem_last < 16;
   const bool lane_row_live = (lane & 15) < rem_last;
   const int voff = lane_row_live ? lane * 16 : TB;
   auto load_slot = [&](int u, int ks) {
@@ -192,7 +195,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
       const uint8_t* at = abase + (size_t)ks * astep + (size_t)b * TB;
-      if (b == MB - 1 && part_last) {
+      if (PAD && b == MB - 1) {
         if constexpr (ADT == FRT_BF16) {
           af[u][b] = Frag<ADT>{};
           if (lane_row_live) load_frag<ADT, false>(af[u][b], at, lane);
@@ -206,6 +209,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
       }
     }
   };
+
   auto mma_slot = [&](int u) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -314,12 +318,17 @@ static hipError_t launch_t(const GemmParams& p, const GemmShape& sh, hipStream_t
     const dim3 grid = sh.row_groups == 1 ? dim3(sh.col_groups, 1, p.splits)
                                          : dim3(8 * sh.row_groups, (sh.col_groups + 7) / 8, p.splits);
     const size_t lds = (size_t)p.kwaves * NT * MB * 64 * sizeof(f32x4);
-    if (sh.fast == kFastPlain)
-      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastPlain>), grid, dim3(256), lds, s, p);
+    const bool pad = p.M % 16 != 0;
+    if (sh.fast == kFastPlain && pad)
+      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastPlain, true>), grid, dim3(256), lds, s, p);
+    else if (sh.fast == kFastPlain)
+      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastPlain, false>), grid, dim3(256), lds, s, p);
+    else if (sh.fast == kFastShape && pad)
+      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastShape, true>), grid, dim3(256), lds, s, p);
     else if (sh.fast == kFastShape)
-      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastShape>), grid, dim3(256), lds, s, p);
+      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastShape, false>), grid, dim3(256), lds, s, p);
     else
-      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kGeneric>), grid, dim3(64 * p.kwaves), lds, s, p);
+      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kGeneric, false>), grid, dim3(64 * p.kwaves), lds, s, p);
     return hipGetLastError();
   }
 }
