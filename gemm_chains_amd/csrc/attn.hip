@@ -381,10 +381,18 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
   Frag<ADT> af[KPH];
 #pragma unroll
   for (int kk = 0; kk < KPH; ++kk) load_frag<ADT, false>(af[kk], opnd + kk * TBA, lane);
-  // The sums pass through LDS and a barrier before the (row-masked) stores: MFMAs ignore
-  // EXEC, and without this the compiler may sink them, and the per-lane scale operands
-  // they read, into the masked store block, where lanes of padding rows hold stale values.
-  __shared__ f32x4 res[4][NTW][64];
+  // The sums go straight from the MFMAs to memory through a buffer resource over this
+  // head's partial slice; lanes of padding rows address past its end, where the hardware
+  // drops the write.  No row-masked branch, which the MFMAs (they ignore EXEC) could be
+  // sunk into, and no pass through LDS and a barrier to prevent that: measured on MI355X
+  // (paired, bitwise equal outputs) -0.17 us/layer at M=50 in bf16, e4m3 and MXFP4, -0.1
+  // at M=10.
+  const int mrow = mb * 16 + (lane & 15);
+  const unsigned slice = (unsigned)(g.M * g.N * 4);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(g.partials + (size_t)h * g.M * g.N), (short)0, (int)slice, kBufferWord3);
+  const bool live = mrow < g.M;
+  const unsigned rowoff = (unsigned)(mrow * g.N * 4);
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     f32x4 acc[KPH];
@@ -393,16 +401,8 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
     f32x4 v = acc[0];
 #pragma unroll
     for (int kk = 1; kk < KPH; ++kk) v += acc[kk];
-    res[wave][t][lane] = v;
-  }
-  __syncthreads();
-  const int mrow = mb * 16 + (lane & 15);
-  if (mrow < g.M) {
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const int n0 = (pt0 + t) * 16 + 4 * (lane >> 4);
-      *reinterpret_cast<f32x4*>(g.partials + ((size_t)h * g.M + mrow) * g.N + n0) = res[wave][t][lane];
-    }
+    const unsigned n0 = (unsigned)((pt0 + t) * 16 + 4 * (lane >> 4));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)(live ? rowoff + 4 * n0 : slice), 0, 0);
   }
 }
 
