@@ -159,6 +159,36 @@ def test_chain_edge_shapes(F, M, prefix, wdtype):
     assert np.array_equal(d["x_out"], got), "production (fused, read-ahead) vs debug chain"
 
 
+@pytest.mark.parametrize("wdtype", ["bf16", "e4m3"])
+def test_chain_wide_hidden(F, wdtype):
+    """A wider model than the pages' action decoder: hidden 2048, 16 query heads over the
+    one KV head, MLP 4096, M=50, 200 cached keys.  Every GEMM gets other tile shapes (the
+    fused merge + O projection 4 column tiles per wave, the down projection's operand 4096
+    wide over 2048 columns), checked teacher-forced and end to end as the 1024-wide chain."""
+    frt, chain = F
+    dims = synth.chain_dims(layers=2, steps=2, M=50, hidden=2048, n_heads=16, prefix=200, mlp=4096)
+    wl = synth.workload4(dims)
+    ws = cp.oracle_weights(wl["layers"], wdtype)
+    adt = "bf16" if wdtype == "bf16" else "e4m3"
+    scales = _oracle_scales(wl, dims) if adt == "e4m3" else None
+    want, sens, bar = _oracle_and_bar(wl, ws, scales, adt)
+    kp, vp = _prefixes(wl)
+    packed = chain.PackedLayers(wl["layers"], dims, frt.DTYPES[wdtype])
+    cd = _run(chain, dims, packed, wl, scales, use_graph=True, keep_intermediates=True)
+    d = cp.gpu_dumps(frt, cd, dims, frt.DTYPES[wdtype])
+    worst = cp.teacher_forced_check(d, wl["x0"], wl["mod"], kp, vp, ws, scales, dims, adt)
+    cd.close()
+    cpf = _run(chain, dims, packed, wl, scales, use_graph=True, prefetch_next=True)
+    got = cpf.read("x_out").reshape(50, -1)
+    cpf.close()
+    err = rel_l2(got, want)
+    log(f"chain {wdtype} hidden 2048, 16 heads: teacher-forced worst {worst}; end to end rel L2 {err:.3e}, "
+        f"oracle sensitivity {sens:.3e}")
+    record(f"chain 2x2 {wdtype} M=50 hidden=2048 heads=16", _figs(worst, err, sens))
+    assert err <= bar
+    assert np.array_equal(d["x_out"], got), "production (fused, read-ahead) vs debug chain"
+
+
 _FULL = {}
 
 
