@@ -355,6 +355,8 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pt0 = 4 * NTW * cg + NTW * wave;   // first column tile of this wave
+  // the operand's static scale, requested first (after the merge it would cost a round trip)
+  const float os = load_scale(p.out_scale_ptr, p.out_scale);
 
   Frag<DT> wf[NTW][KPH];
 #pragma unroll
@@ -368,7 +370,6 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
   const int d0 = (threadIdx.x & 15) * 8;
   float o[8];
   merge_records<CH>(p, h, mb, MB, nch, tq, d0, mb * 16 + tq < p.M, o);
-  const float os = load_scale(p.out_scale_ptr, p.out_scale);
   const int m = mb * 16 + tq;
   store_operand4(opnd, ADT, 1, tq, d0, o[0], o[1], o[2], o[3], os, m >= p.M);
   store_operand4(opnd, ADT, 1, tq, d0 + 4, o[4], o[5], o[6], o[7], os, m >= p.M);
