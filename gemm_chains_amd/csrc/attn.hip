@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
   constexpr int TBW = tile_bytes_of(DT), TBA = tile_bytes_of(ADT);
   constexpr int KPH = HD / kstep_of(DT);  // k-steps per head: 4 (bf16) or 1 (e4m3, MXFP4)
   __shared__ __attribute__((aligned(16))) uint8_t opnd[KPH * TBA];
-  const int h = blockIdx.x, mb = blockIdx.y, cg = blockIdx.z, MB = gridDim.y;
+  const int h = blockIdx.x, mb = blockIdx.y, cg = blockIdx.z, MB = p.MB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pt0 = 4 * NTW * cg + NTW * wave;   // first column tile of this wave
@@ -365,6 +365,19 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
     for (int kk = 0; kk < KPH; ++kk)
       load_frag<DT, true>(wf[t][kk], g.w + ((size_t)(pt0 + t) * g.ksteps + h * KPH + kk) * TBW, lane);
   __builtin_amdgcn_sched_barrier(0);  // the weight loads go out first
+  // Then every kernel argument that addresses the records, in one batch of scalar loads
+  // (the empty asm only makes these values live here).  Read where the merge first uses
+  // them, they came in two dependent scalar round trips ahead of the record loads (their
+  // cache lines hold nothing the weight loads use; MB came from gridDim.y, an implicit
+  // argument on a line of its own).  Measured on MI355X (paired, bitwise equal outputs,
+  // with the Q/K/V scatter's arguments in the QKV GEMM): -0.08 / -0.25 us per layer
+  // (bf16, M=50 / 10), -0.03 / -0.20 (e4m3), -0.13 / -0.23 (MXFP4 weights).  Requested at
+  // kernel start instead, they held back the weight loads: +0.1 us for MXFP4 at M=50.
+  {
+    const int pm = p.M, pnh = p.n_heads;
+    const float* pws = p.workspace;
+    asm volatile("" ::"s"(pm), "s"(pnh), "s"(pws), "s"(nch), "s"(MB));
+  }
 
   const int tq = threadIdx.x >> 4;
   const int d0 = (threadIdx.x & 15) * 8;

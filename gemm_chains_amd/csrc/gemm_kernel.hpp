@@ -251,6 +251,13 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
 #pragma unroll
   for (int u = 0; u < PER; ++u) load_slot(u, ks_begin + u);
   __builtin_amdgcn_sched_barrier(0);
+  // The Q/K/V scatter's pointers and sizes share no kernel-argument cache line with what
+  // the loads use.  Requested here (the empty asm only makes them live), their scalar
+  // round trip overlaps the loads in flight; read at their first use, it came after the
+  // MFMAs, at the very end of the kernel.
+  if constexpr (EPI == kGemmQkv) {
+    asm volatile("" ::"s"(p.q_out), "s"(p.k_out), "s"(p.v_out), "s"(p.nq), "s"(p.hd), "s"(p.v_ld));
+  }
   if constexpr (!SHAPE) {
     // Rolling pipeline over the further rounds: as soon as slot u's MFMAs have read it,
     // the slot is reloaded with the same slot of the next round, so a full round of loads
