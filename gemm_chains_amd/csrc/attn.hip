@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
   // argument on a line of its own).  Measured on MI355X (paired, bitwise equal outputs,
   // with the Q/K/V scatter's arguments in the QKV GEMM): -0.08 / -0.25 us per layer
   // (bf16, M=50 / 10), -0.03 / -0.20 (e4m3), -0.13 / -0.23 (MXFP4 weights).  Requested at
-  // kernel start instead, they held back the weight loads: +0.1 us for MXFP4 at M=50.
+  // kernel start instead, in the weights' batch: the same within 0.04 us.
   {
     const int pm = p.M, pnh = p.n_heads;
     const float* pws = p.workspace;
