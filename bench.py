@@ -346,7 +346,15 @@ def state_reuse(torch, chain, synth, dims, packed, wl, reps=20):
 
 # MI355X dense, published.  MXFP4 weights meet e4m3 activations in the FP4 x FP8 form of the
 # block-scaled MFMA, which runs at the FP8 rate, so its peak is FP8's.
+# dense MFMA peaks of the instruction each path runs: bf16 MFMA for bf16 weights, the fp8
+# MFMA for e4m3 x e4m3 (but the bf16 MFMA at M <= 16, where the codes are multiplied as
+# bf16 for exact products: mfma_peak_tflops), the FP4 x FP8 block-scaled MFMA (fp8 rate)
+# for MXFP4 weights
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "mxfp4": 5000.0}
+
+
+def mfma_peak_tflops(name, M):
+    return MFMA_PEAK_TFLOPS["bf16"] if name == "e4m3" and M <= 16 else MFMA_PEAK_TFLOPS[name]
 
 
 def gemm_sweep(torch, frt, device, synth):
@@ -358,7 +366,7 @@ def gemm_sweep(torch, frt, device, synth):
         for M in (1, 10, 16, 32, 50, 64):
             us, nbytes, s = time_gemm(torch, frt, device, synth, M, K, N, dt, reps=64)
             gbs = nbytes / (us * 1e-6) / 1e9
-            util = 2.0 * M * K * N / (us * 1e-6) / (MFMA_PEAK_TFLOPS[name] * 1e12)
+            util = 2.0 * M * K * N / (us * 1e-6) / (mfma_peak_tflops(name, M) * 1e12)
             rows.append(dict(M=M, dtype=name, splits=s, us=round(us, 3), gbs=round(gbs, 1),
                              hbm_frac=round(gbs / HBM_PEAK_GBS, 4), mfma_util=round(util, 5)))
             log(f"sweep K={K} N={N} M={M} {name}: {us:.2f} us, {gbs:.0f} GB/s, MFMA {util:.2%}")

@@ -350,7 +350,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const AttnParams p, i
 // as the O GEMM with one split per head adds its waves' sums, so the partials are
 // bitwise those of the merge kernel followed by that GEMM.  The weight loads are issued
 // first and overlap the record loads.
-template <int DT, int CH, int NTW>
+template <int DT, int CH, int NTW, bool EXACT = false>
 __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams p, const GemmParams g, int nch) {
   constexpr int ADT = act_dtype_of(DT);
   constexpr int TBW = tile_bytes_of(DT), TBA = tile_bytes_of(ADT);
@@ -416,7 +416,7 @@ __global__ void __launch_bounds__(256) attn_merge_oproj_kernel(const AttnParams 
   for (int t = 0; t < NTW; ++t) {
     f32x4 acc[KPH];
 #pragma unroll
-    for (int kk = 0; kk < KPH; ++kk) acc[kk] = mma(wf[t][kk], af[kk], f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int kk = 0; kk < KPH; ++kk) acc[kk] = mma_sel<EXACT>(wf[t][kk], af[kk], f32x4{0.f, 0.f, 0.f, 0.f});
     f32x4 v = acc[0];
 #pragma unroll
     for (int kk = 1; kk < KPH; ++kk) v += acc[kk];
@@ -478,23 +478,31 @@ hipError_t launch_attention_oproj(const AttnParams& p_in, const GemmParams& g, h
   // record slots per thread: the exact chunk count up to 8 (a slot past the last chunk
   // still costs its loads: 8 slots for the 7 chunks of M=50 cost 0.18 us per layer,
   // paired), 16 above that
-#define FRT_MERGE_OPROJ(DT, CH) \
-  by_ntw(attn_merge_oproj_kernel<DT, CH, 1>, attn_merge_oproj_kernel<DT, CH, 2>, attn_merge_oproj_kernel<DT, CH, 4>)
-#define FRT_MERGE_OPROJ_DT(DT)                         \
+  // e4m3 x e4m3 products exact at M <= 16, as in the O GEMM (the two stay bitwise equal)
+#define FRT_MERGE_OPROJ(DT, CH, X)                                                                    \
+  by_ntw(attn_merge_oproj_kernel<DT, CH, 1, X>, attn_merge_oproj_kernel<DT, CH, 2, X>, \
+         attn_merge_oproj_kernel<DT, CH, 4, X>)
+#define FRT_MERGE_OPROJ_DT(DT, X)                      \
   switch (nch) {                                       \
-    case 2: FRT_MERGE_OPROJ(DT, 2); break;             \
-    case 3: FRT_MERGE_OPROJ(DT, 3); break;             \
-    case 4: FRT_MERGE_OPROJ(DT, 4); break;             \
-    case 5: FRT_MERGE_OPROJ(DT, 5); break;             \
-    case 6: FRT_MERGE_OPROJ(DT, 6); break;             \
-    case 7: FRT_MERGE_OPROJ(DT, 7); break;             \
-    case 8: FRT_MERGE_OPROJ(DT, 8); break;             \
-    default: FRT_MERGE_OPROJ(DT, 16); break;           \
+    case 2: FRT_MERGE_OPROJ(DT, 2, X); break;          \
+    case 3: FRT_MERGE_OPROJ(DT, 3, X); break;          \
+    case 4: FRT_MERGE_OPROJ(DT, 4, X); break;          \
+    case 5: FRT_MERGE_OPROJ(DT, 5, X); break;          \
+    case 6: FRT_MERGE_OPROJ(DT, 6, X); break;          \
+    case 7: FRT_MERGE_OPROJ(DT, 7, X); break;          \
+    case 8: FRT_MERGE_OPROJ(DT, 8, X); break;          \
+    default: FRT_MERGE_OPROJ(DT, 16, X); break;        \
   }
   switch (g.ab_dtype) {
-    case FRT_BF16: FRT_MERGE_OPROJ_DT(FRT_BF16); break;
-    case FRT_E4M3: FRT_MERGE_OPROJ_DT(FRT_E4M3); break;
-    default: FRT_MERGE_OPROJ_DT(FRT_MXFP4); break;
+    case FRT_BF16: FRT_MERGE_OPROJ_DT(FRT_BF16, false); break;
+    case FRT_E4M3:
+      if (e4m3_exact(g.M)) {
+        FRT_MERGE_OPROJ_DT(FRT_E4M3, true);
+      } else {
+        FRT_MERGE_OPROJ_DT(FRT_E4M3, false);
+      }
+      break;
+    default: FRT_MERGE_OPROJ_DT(FRT_MXFP4, false); break;
   }
 #undef FRT_MERGE_OPROJ_DT
 #undef FRT_MERGE_OPROJ

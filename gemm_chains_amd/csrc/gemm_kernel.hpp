@@ -17,6 +17,7 @@
 // code of its own epilogue (a template parameter): a long branchy tail costs fetch
 // latency on every launch.
 #pragma once
+#include <type_traits>
 #include "frt_internal.hpp"
 
 namespace frt {
@@ -97,6 +98,42 @@ __device__ __forceinline__ f32x4 mma(const Frag<FRT_E4M3>& w, const Frag<FRT_E4M
   // format 0/0 = OCP e4m3 for both operands; E8M0 block scales 127 = 2^0 (unscaled)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, aa, c, 0, 0, 0, 127, 0, 127);
 }
+// e4m3 x e4m3 with exact products: a lane's 32 codes of the 128-wide k-step are four groups
+// of 8, each decoded to bf16 (every e4m3 value is a bf16 value, so the decode is exact) and
+// multiplied by a bf16 MFMA, whose products are exact and whose sums are fp32.  Weights
+// and activations take the same groups, so the four MFMAs add each of the 128 products
+// once.  The fp8 MFMA above keeps about 13 bits of its internal sum: against the float64
+// oracle its partial sums are off by about 1.5e-5 (relative), and through flipped e4m3
+// codes config 3's SiLU output by 2.6e-3, over its stated 2e-3; exact, 4.5e-8 and 0.
+// Kernels take this form when M <= 16, where every workgroup holds one 16-row block and
+// the extra MFMAs and conversions are cheap: measured on MI355X (paired), +0.40 us per
+// layer of the e4m3 chain at M=10.  With four row blocks they are not: at M=50 the chain
+// lost 0.72 us per layer and the K=2048, N=16384 gate|up GEMM went from 9.8 to 12.9 us,
+// so M > 16 keeps the fp8 MFMA.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo4, uint32_t hi4) {
+  const u32x4 r = {e4m3x2_to_bf16x2<false>(lo4), e4m3x2_to_bf16x2<true>(lo4), e4m3x2_to_bf16x2<false>(hi4),
+                   e4m3x2_to_bf16x2<true>(hi4)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ f32x4 mma_exact(const Frag<FRT_E4M3>& w, const Frag<FRT_E4M3>& a, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(w.v0.x, w.v0.y), e4m3x8_to_bf16(a.v0.x, a.v0.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(w.v0.z, w.v0.w), e4m3x8_to_bf16(a.v0.z, a.v0.w), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(w.v1.x, w.v1.y), e4m3x8_to_bf16(a.v1.x, a.v1.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(w.v1.z, w.v1.w), e4m3x8_to_bf16(a.v1.z, a.v1.w), c, 0, 0, 0);
+  return c;
+}
+// EXACT selects mma_exact (e4m3 weights and activations only)
+template <bool EXACT, int WDT, int ADT>
+__device__ __forceinline__ f32x4 mma_sel(const Frag<WDT>& w, const Frag<ADT>& a, f32x4 c) {
+  if constexpr (EXACT) return mma_exact(w, a, c);
+  else return mma(w, a, c);
+}
+// e4m3 x e4m3 products are exact when M <= 16 (the row count of the whole GEMM)
+inline bool e4m3_exact(int M) { return M <= 16; }
 __device__ __forceinline__ f32x4 mma(const Frag<FRT_MXFP4>& w, const Frag<FRT_E4M3>& a, f32x4 c) {
   i32x8 wa, aa;
   wa[0] = (int)w.v.x; wa[1] = (int)w.v.y; wa[2] = (int)w.v.z; wa[3] = (int)w.v.w;
@@ -127,7 +164,7 @@ __device__ __forceinline__ float silu_f(float g) {
 // FAST (GemmFast) fixes four waves and a single round, and with kFastPlain drops the
 // pointer-read scales: measured on MI355X, the shorter, branch-free code saves 0.4 us per
 // launch of the gate|up GEMM.
-template <int DT, int MB, int NT, int PER, int EPI, int FAST, bool PAD>
+template <int DT, int MB, int NT, int PER, int EPI, int FAST, bool PAD, bool EXACT = false>
 __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
   constexpr bool SHAPE = FAST != kGeneric, PLAIN = FAST == kFastPlain;
   constexpr int ADT = act_dtype_of(DT);   // operand (activation) format
@@ -214,7 +251,7 @@ __global__ void __launch_bounds__(256) skinny_gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int b = 0; b < MB; ++b) acc[t][b] = mma(wf[u][t], af[u][b], acc[t][b]);
+      for (int b = 0; b < MB; ++b) acc[t][b] = mma_sel<EXACT>(wf[u][t], af[u][b], acc[t][b]);
   };
   // With e4m3 weights the epilogue's scales are requested ahead of the k-step loads:
   // after the sums, the scalar scale loads and the column-scale loads each cost a memory
@@ -366,16 +403,26 @@ static hipError_t launch_t(const GemmParams& p, const GemmShape& sh, hipStream_t
                                          : dim3(8 * sh.row_groups, (sh.col_groups + 7) / 8, p.splits);
     const size_t lds = (size_t)p.kwaves * NT * MB * 64 * sizeof(f32x4);
     const bool pad = p.M % 16 != 0;
-    if (sh.fast == kFastPlain && pad)
-      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastPlain, true>), grid, dim3(256), lds, s, p);
-    else if (sh.fast == kFastPlain)
-      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastPlain, false>), grid, dim3(256), lds, s, p);
-    else if (sh.fast == kFastShape && pad)
-      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastShape, true>), grid, dim3(256), lds, s, p);
-    else if (sh.fast == kFastShape)
-      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastShape, false>), grid, dim3(256), lds, s, p);
-    else
-      hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kGeneric, false>), grid, dim3(64 * p.kwaves), lds, s, p);
+    auto go = [&](auto exact) {
+      constexpr bool X = decltype(exact)::value;
+      if (sh.fast == kFastPlain && pad)
+        hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastPlain, true, X>), grid, dim3(256), lds, s, p);
+      else if (sh.fast == kFastPlain)
+        hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastPlain, false, X>), grid, dim3(256), lds, s, p);
+      else if (sh.fast == kFastShape && pad)
+        hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastShape, true, X>), grid, dim3(256), lds, s, p);
+      else if (sh.fast == kFastShape)
+        hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kFastShape, false, X>), grid, dim3(256), lds, s, p);
+      else
+        hipLaunchKernelGGL((skinny_gemm_kernel<DT, MB, NT, PER, EPI, kGeneric, false, X>), grid, dim3(64 * p.kwaves), lds, s,
+                           p);
+    };
+    if constexpr (DT == FRT_E4M3 && MB == 1) {
+      if (e4m3_exact(p.M)) go(std::true_type{});
+      else go(std::false_type{});
+    } else {
+      go(std::false_type{});
+    }
     return hipGetLastError();
   }
 }

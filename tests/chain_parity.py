@@ -9,7 +9,8 @@ inputs to that kernel* (teacher forcing), at the per-kernel bars:
                                  QKV operand codes within the tie band
   QKV GEMM + split               Q, own K, own V bf16 codes within the tie band
   attention                      O-projection operand codes within the tie band
-  O projection                   fp32 partials, relative L2 <= 1e-5 (bf16) / 1e-4 (fp8)
+  O projection                   fp32 partials, relative L2 <= 1e-5 where the products are
+                                 exact (bf16; e4m3 at M <= 16), else 1e-4
   producer (MLP sublayer)        h_mlp as above; gate|up operand codes within the tie band
   gate|up GEMM + SiLU gate       down-projection operand codes within the tie band
   down projection                fp32 partials as for the O projection
@@ -31,17 +32,14 @@ reduced by the consumer).
 import numpy as np
 
 from oracle import codec, ref
-from tests.helpers import check_codes, rel_l2, silu_gate_mag
+from tests.helpers import check_codes, e4m3_products_exact, partial_bar, rel_l2, silu_gate_mag
 
 SITE_QKV, SITE_O, SITE_UP, SITE_DOWN = 0, 1, 2, 3
 SCALE, SHIFT, GATE = 0, 1, 2
 RES_ULPS = 2.0 ** -20          # residual-stream bound, relative to the size of its summands
 
 
-def _partial_bar(adt):
-    # fp8 x fp8 (and FP4 x FP8) MFMAs sum their products inside the instruction with less
-    # than fp32 precision (about 1.5e-5 relative measured); bf16 products are exact
-    return 1e-5 if adt == "bf16" else 1e-4
+
 
 
 def _splits_from_bytes(total, SL, one):
@@ -113,18 +111,22 @@ def _check_residual(got, want, r, gate, xmag, label):
                              f"gpu {got.ravel()[i]!r} oracle {want.ravel()[i]!r} (rel L2 {rel_l2(got, want):.2e})")
 
 
-def teacher_forced_check(dumps, x0, mod, kp, vp, ws, scales, dims, adt, steps=None, eps=1e-6, log=None):
+def teacher_forced_check(dumps, x0, mod, kp, vp, ws, scales, dims, adt, steps=None, eps=1e-6, log=None,
+                         wdtype=None):
     """Check every kernel of every listed flow step against the oracle on the GPU's own
     inputs.  ws: per-layer oracle weights (decoded values; colscales 's<name>' for e4m3
-    weights); scales: [L][4] static activation scales (e4m3 activations) or None.
+    weights); scales: [L][4] static activation scales (e4m3 activations) or None;
+    wdtype: the weight format ("bf16", "e4m3" or "mxfp4"; default: that of adt).
     Raises AssertionError naming the first (step, layer, kernel) that fails; returns a
     dict of the worst figure per check."""
     S, L, M, H = dims["steps"], dims["layers"], dims["M"], dims["hidden"]
     nh, hd = dims["n_heads"], dims["head_dim"]
     nq = nh * hd
     steps = range(S) if steps is None else steps
-    qkv_frac = 0.01 if adt == "bf16" else 0.05   # bf16 roundings of fp8-GEMM outputs (MFMA rounding)
-    pbar = _partial_bar(adt)
+    wdtype = wdtype or adt
+    exact = wdtype == "bf16" or (wdtype == "e4m3" and e4m3_products_exact(M))
+    qkv_frac = 0.01 if exact else 0.05   # bf16 roundings of fp8-MFMA outputs (its internal rounding)
+    pbar = partial_bar(wdtype, M)
     worst = dict(h=0.0, p_o=0.0, p_down=0.0, code_frac=0.0)
     dec = lambda c: codec.decode(c, adt)  # noqa: E731
 

@@ -18,10 +18,9 @@ the same seeded inputs (it never reads a GPU output).  Bars:
   - codes that a GEMM epilogue rounds (the SiLU-gate output) are checked teacher-forced:
     the GPU GEMM is fed the oracle's operand codes (host-packed) and its codes must match
     up to the tie band; end to end (on the GPU's own operand) their decoded values must
-    stay within the GEMM-output bar, except in the FP8 block, where one-step flips of
-    downstream e4m3 codes that the tie band allows dominate: there the end-to-end bar is
-    twice the oracle's own sensitivity (2^-17 relative noise on the producer's values),
-    and the test prints whether the stated 2e-3 is met.
+    stay within the GEMM-output bar (2e-3 in the FP8 block).  The test also prints the
+    oracle's own sensitivity there (2^-17 relative noise on the producer's values), for
+    scale: one flipped e4m3 code moves a whole column of the next GEMM.
 """
 import math
 
@@ -221,10 +220,11 @@ def test_config3_fp8_static_scale_block(F):
     c = _gemm_f32(frt, dev, M, K, Fm, 4, E, frt.W_PLAIN, zo, wd, cd, s_z)
     torch.cuda.synchronize()
     # End to end, a tie-band difference in one e4m3 operand code moves a whole column of
-    # the next GEMM, so downstream e4m3 codes can flip by a step (1/16 of a value).  The bar
-    # is the oracle's own sensitivity (as for the chain): perturb the producer's values by
-    # the tie-band width (2^-17 relative) before rounding, rerun the oracle, and allow twice
-    # the change that causes.
+    # the next GEMM, so downstream e4m3 codes can flip by a step (1/16 of a value).  The
+    # GEMMs' exact products leave such flips to the rare values within an fp32 rounding of
+    # a midpoint; the stated bar applies.  The oracle's own sensitivity is printed for
+    # scale: the producer's values perturbed by the tie-band width (2^-17 relative) before
+    # rounding, and the oracle rerun.
     g = np.random.default_rng(3)
     vp = o["v"] * (1.0 + 2.0 ** -17 * g.standard_normal(o["v"].shape))
     a_p = codec.e4m3_decode(codec.e4m3_encode(vp))
@@ -234,17 +234,11 @@ def test_config3_fp8_static_scale_block(F):
     e2e_z, e2e = rel_l2(dec(zc[:M]), z["deq"]), rel_l2(dev.to_np(c), c_down)
     print(f"config 3 end to end: SiLU output rel L2 {e2e_z:.2e} (oracle sensitivity {sens_z:.2e}), "
           f"down rel L2 {e2e:.2e} (sensitivity {sens_d:.2e})")
-    # The stated fp8 bar (2e-3) holds for every GEMM output teacher-forced (above and
-    # below).  End to end, the one-step flips of downstream e4m3 codes that the tie band
-    # allows dominate (about 2.6e-3 measured against 2e-3): that leg passes only under the
-    # sensitivity reading (twice the oracle's own change), and the print says which.
-    print(f"config 3 end to end vs the stated 2e-3: SiLU {'meets' if e2e_z <= 2e-3 else 'MISSES'}, "
-          f"down {'meets' if e2e <= 2e-3 else 'MISSES'}")
-    record("config 3 fp8 end to end", f"SiLU {e2e_z:.2e}, down {e2e:.2e} against the stated 2e-3 "
-                                      f"({'met' if max(e2e_z, e2e) <= 2e-3 else 'MISSED'}; passes under 2 x oracle "
-                                      f"sensitivity {sens_z:.2e} / {sens_d:.2e})")
-    assert e2e_z <= 2 * sens_z, "config 3 SiLU end to end"
-    assert e2e <= 2 * sens_d, "config 3 down end to end"
+    record("config 3 fp8 end to end", f"SiLU {e2e_z:.2e}, down {e2e:.2e} (bar 2e-3; oracle sensitivity "
+                                      f"{sens_z:.2e} / {sens_d:.2e})")
+    assert e2e_z <= 2e-3, "config 3 SiLU end to end"
+    assert e2e <= 2e-3, "config 3 down end to end"
+
     # teacher-forced down projection
     a_pk = dev.to_dev(frt.frt_operand_pack_host(z["codes"], E, M, Fm))
     c = _gemm_f32(frt, dev, M, K, Fm, 4, E, frt.W_PLAIN, a_pk, wd, cd, s_z)

@@ -5,9 +5,10 @@ the oracle, through the C ABI (MI355X only).
   E8M0 exponent and rounds every element once, as the oracle does, so codes and scale
   bytes are bit-exact; hand-made blocks pin the FP4 tie and saturation rules, an all-zero
   block and the exponent clamp.
-- GEMM: FP4 x FP8 products are exact and the block scales are powers of two, so the
-  float32 partials are held to the same bar as the e4m3 GEMM (relative L2 1e-4 of the
-  float64 products of the decoded values).  The weights' per-block magnitudes differ by
+- GEMM: FP4 x FP8 products are exact and the block scales are powers of two, but the
+  block-scaled MFMA sums its products inside the instruction with less than fp32
+  precision (about 1.5e-5 relative measured), so the float32 partials are held to
+  relative L2 1e-4 of the float64 products of the decoded values.  The weights' per-block magnitudes differ by
   up to 2^12, so a block paired with the wrong scale or the wrong activations is far
   outside that bar.
 - Epilogues (store, SiLU-gate quantisation, fused QKV scatter) run on the same sums:
