@@ -176,6 +176,8 @@ GEMM_CASES = [
     (50, 1280, 1024, "e4m3", 4), (64, 16384, 2048, "bf16", 2), (1, 16384, 2048, "e4m3", 4),
     (1, 16, 32, "bf16", 1), (17, 48, 96, "bf16", 1), (33, 32, 128, "e4m3", 1),
     (64, 64, 512, "bf16", 16), (49, 1024, 1024, "e4m3", 8),
+    # either side of the e4m3 product switch: exact products up to 16 rows, the fp8 MFMA above
+    (16, 2560, 1024, "e4m3", 2), (17, 1024, 1024, "e4m3", 1),
 ]
 
 
