@@ -591,8 +591,10 @@ def main():
                     help="print the launch-gap shares of the chain's decisions in a rocprofv3 kernel-trace CSV "
                          "(of a --chain-only run) as JSON, and exit (no GPU needed)")
     ap.add_argument("--chain-only", action="store_true",
-                    help="run only the M=50 bf16 chain (read-ahead on) for --warmup + --steps decisions "
-                         "(the program the launch-gap kernel trace profiles)")
+                    help="run only the bf16 chain (M=50 unless --rows says otherwise; read-ahead on) for "
+                         "--warmup + --steps decisions (the program the launch-gap kernel trace profiles)")
+    ap.add_argument("--rows", type=int, default=50, choices=(10, 50),
+                    help="action rows M of the --chain-only chain")
     args = ap.parse_args()
     if args.analyze_trace:
         res = analyze_chain_trace(args.analyze_trace)
@@ -616,14 +618,14 @@ def main():
         return
 
     if args.chain_only:
-        dims = synth.chain_dims(layers=args.layers, steps=args.flow_steps, M=50)
+        dims = synth.chain_dims(layers=args.layers, steps=args.flow_steps, M=args.rows)
         wl = synth.workload4(dims)
         packed = chain.PackedLayers(wl["layers"], dims, frt.BF16)
         ch = chain.Chain(dims, packed, use_graph=True, prefetch_next=True)
         chain.load_workload(ch, wl)
         torch.cuda.synchronize()
         ms = time_chain(torch, ch, args.steps, args.warmup)
-        print(json.dumps({"chain_us_per_layer_m50_bf16": round(ms * 1e3 / (dims["layers"] * dims["steps"]), 3),
+        print(json.dumps({f"chain_us_per_layer_m{args.rows}_bf16": round(ms * 1e3 / (dims["layers"] * dims["steps"]), 3),
                           "decisions": args.warmup + args.steps, "kernels_per_decision": ch.kernel_count()}),
               flush=True)
         ch.close()
