@@ -89,7 +89,7 @@ def silu_gate_mag(c, a_dec, w_dec, act, s_w, dtype, out_scale):
 
 
 class Canaries:
-    """Device buffers with PAD canary bytes on each side (SURVEY's canary-guarded outputs):
+    """Device buffers with PAD canary bytes on each side (canary-guarded outputs):
     `bytes` / `f32` hand out the inner region, `check` asserts that no kernel wrote past
     either end of any buffer handed out."""
     PAD = 256

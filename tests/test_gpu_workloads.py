@@ -1,13 +1,13 @@
 """GPU parity of the four stand-alone workloads, composed the way each is described, against
 the oracle (MI355X only).
 
-  1  fused residual + RMSNorm + bf16 GEMM, M=10, K=N=1024, gamma folded into W, s in {1,2,4}
-  2  gated MLP at M=50: up (1024 -> 8192 gate|up) + SiLU gate, then down (4096 -> 1024),
-     s in {1,2,4,8} per GEMM
-  3  FP8 static-scale block at M=10: gated residual + AdaRMSNorm -> e4m3, fused QKV
-     (1024 -> 2560), gate|up (1024 -> 8192) + SiLU gate -> e4m3, down (4096 -> 1024)
-  5  gate|up GEMM sweep, K=2048, N=16384, M in {1,10,16,32,50,64}, bf16 and e4m3,
-     split-K from the library's table
+  - fused residual + RMSNorm + bf16 GEMM, M=10, K=N=1024, gamma folded into W, s in {1,2,4}
+  - gated MLP at M=50: up (1024 -> 8192 gate|up) + SiLU gate, then down (4096 -> 1024),
+    s in {1,2,4,8} per GEMM
+  - FP8 static-scale block at M=10: gated residual + AdaRMSNorm -> e4m3, fused QKV
+    (1024 -> 2560), gate|up (1024 -> 8192) + SiLU gate -> e4m3, down (4096 -> 1024)
+  - gate|up GEMM sweep, K=2048, N=16384, M in {1,10,16,32,50,64}, bf16 and e4m3,
+    split-K from the library's table
 
 Every GPU step runs on the GPU's own upstream outputs; the oracle runs its own pipeline on
 the same seeded inputs (it never reads a GPU output).  Bars:
@@ -89,7 +89,7 @@ def _mp(M):
 
 # ------------------------------------------------------------------ workload 1
 
-def test_config1_fused_rmsnorm_bf16_gemm(F):
+def test_fused_rmsnorm_bf16_gemm_m10(F):
     frt, dev = F
     w1 = synth.workload1()
     M, K, N, eps = w1["M"], w1["K"], w1["N"], w1["eps"]
@@ -99,7 +99,7 @@ def test_config1_fused_rmsnorm_bf16_gemm(F):
     # oracle: producer codes, W' = bf16(diag(gamma) W), and the emulating GEMM
     o = ref.residual_norm_quant(w1["r"], w1["x"][None], None, 1.0, None, None, None, eps, "bf16")
     wcodes, _, _ = ref.pack_weight_values(codec.bf16_decode(w1["w"]), w1["gamma"], "bf16")
-    check_codes(dev.operand_codes(op, frt.BF16, _mp(M), K)[:M], o["v"], o["mag"], "bf16", label="config 1 operand")
+    check_codes(dev.operand_codes(op, frt.BF16, _mp(M), K)[:M], o["v"], o["mag"], "bf16", label="rmsnorm+gemm M=10 operand")
     assert np.array_equal(dev.weight_codes(wp, frt.BF16, K, N), wcodes), "W' = bf16(diag(gamma) W), rounded once"
     c_emul = ref.reduce_partials(ref.gemm_splitk(o["deq"], codec.bf16_decode(wcodes), 1))
     # the plain definition y = (xhat * gamma) W that the fused path reaches
@@ -118,9 +118,9 @@ def test_config1_fused_rmsnorm_bf16_gemm(F):
         assert rel_l2(outs[s], c_plain) <= 5e-3, f"s={s} vs plain definition"
         bf = codec.bf16_decode(cb.cpu().numpy().view(np.uint16))
         assert rel_l2(bf, c_emul) <= 5e-3, f"s={s} bf16 output"
-        print(f"config 1 s={s}: rel L2 vs emulating {rel_l2(outs[s], c_emul):.2e}, vs plain "
+        print(f"rmsnorm+gemm M=10 s={s}: rel L2 vs emulating {rel_l2(outs[s], c_emul):.2e}, vs plain "
               f"{rel_l2(outs[s], c_plain):.2e}")
-        record(f"config 1 bf16 s={s}", f"C vs emulating {rel_l2(outs[s], c_emul):.2e} (bar 5e-3), "
+        record(f"rmsnorm+gemm M=10 bf16 s={s}", f"C vs emulating {rel_l2(outs[s], c_emul):.2e} (bar 5e-3), "
                                        f"vs plain definition {rel_l2(outs[s], c_plain):.2e}")
     for s in (2, 4):
         assert rel_l2(outs[s], outs[1]) <= 1e-5, f"split {s} vs unsplit"
@@ -128,7 +128,7 @@ def test_config1_fused_rmsnorm_bf16_gemm(F):
 
 # ------------------------------------------------------------------ workload 2
 
-def test_config2_gated_mlp_bf16(F):
+def test_gated_mlp_bf16_m50(F):
     frt, dev = F
     w2 = synth.workload2()
     M, K, Fm, eps = w2["M"], w2["K"], w2["mlp"], w2["eps"]
@@ -142,28 +142,28 @@ def test_config2_gated_mlp_bf16(F):
     z = ref.silu_gate_quant(c_up, "bf16")
     c_down = ref.reduce_partials(ref.gemm_splitk(z["deq"], wd_v, 1))
     torch.cuda.synchronize()
-    check_codes(dev.operand_codes(op, frt.BF16, _mp(M), K)[:M], o["v"], o["mag"], "bf16", label="config 2 operand")
+    check_codes(dev.operand_codes(op, frt.BF16, _mp(M), K)[:M], o["v"], o["mag"], "bf16", label="gated MLP M=50 operand")
     zs = {}
     for s in (1, 2, 4, 8):
         _silu_teacher_forced(frt, dev, M, N_up, K, s, frt.BF16, "bf16", o, wu, None, wu_v, None, 1.0, 1.0,
-                             f"config 2 SiLU s={s}")
+                             f"gated MLP M=50 SiLU s={s}")
         out = _silu(frt, dev, M, N_up, K, s, frt.BF16, op, wu, None, 1.0, 1.0)
         torch.cuda.synchronize()
         zc = dev.operand_codes(out, frt.BF16, _mp(M), Fm)
         assert np.all(zc[M:] == 0)
         zs[s] = out
         e2e = rel_l2(codec.bf16_decode(zc[:M]), z["deq"])
-        assert e2e <= 5e-3, f"config 2 SiLU s={s} end to end"
-        print(f"config 2 up s={s}: SiLU output rel L2 end to end {e2e:.2e}")
-        record(f"config 2 bf16 gate|up s={s}", f"SiLU output end to end {e2e:.2e} (bar 5e-3)")
+        assert e2e <= 5e-3, f"gated MLP M=50 SiLU s={s} end to end"
+        print(f"gated MLP M=50 up s={s}: SiLU output rel L2 end to end {e2e:.2e}")
+        record(f"gated MLP M=50 bf16 gate|up s={s}", f"SiLU output end to end {e2e:.2e} (bar 5e-3)")
     downs = {}
     for s in (1, 2, 4, 8):
         c = _gemm_f32(frt, dev, M, K, Fm, s, frt.BF16, frt.W_PLAIN, zs[1], wd, None, 1.0)
         torch.cuda.synchronize()
         downs[s] = dev.to_np(c)
         assert rel_l2(downs[s], c_down) <= 5e-3, f"down s={s}"
-        print(f"config 2 down s={s}: rel L2 {rel_l2(downs[s], c_down):.2e}")
-        record(f"config 2 bf16 down s={s}", f"C end to end {rel_l2(downs[s], c_down):.2e} (bar 5e-3)")
+        print(f"gated MLP M=50 down s={s}: rel L2 {rel_l2(downs[s], c_down):.2e}")
+        record(f"gated MLP M=50 bf16 down s={s}", f"C end to end {rel_l2(downs[s], c_down):.2e} (bar 5e-3)")
     for s in (2, 4, 8):
         assert rel_l2(downs[s], downs[1]) <= 1e-5, f"down split {s} vs unsplit"
     # teacher-forced down projection: the oracle's SiLU codes, host-packed
@@ -175,7 +175,7 @@ def test_config2_gated_mlp_bf16(F):
 
 # ------------------------------------------------------------------ workload 3
 
-def test_config3_fp8_static_scale_block(F):
+def test_fp8_static_scale_block_m10(F):
     frt, dev = F
     w3 = synth.workload3()
     cal = synth.workload3(seed=synth.CAL_SEED)
@@ -200,7 +200,7 @@ def test_config3_fp8_static_scale_block(F):
     z = ref.silu_gate_quant(c_up, "e4m3", s_z)
     c_down = ref.reduce_partials(ref.gemm_splitk(z["deq"], dec(dc), 1), s_z, ds)
     torch.cuda.synchronize()
-    check_codes(dev.operand_codes(op, E, _mp(M), K)[:M], o["v"], o["mag"], "e4m3", label="config 3 operand")
+    check_codes(dev.operand_codes(op, E, _mp(M), K)[:M], o["v"], o["mag"], "e4m3", label="FP8 block M=10 operand")
     assert np.array_equal(dev.to_np(cq).astype(np.float64), qs)
     assert np.array_equal(dev.to_np(cu).astype(np.float64), us)
     qkv = {}
@@ -209,10 +209,10 @@ def test_config3_fp8_static_scale_block(F):
         torch.cuda.synchronize()
         qkv[s] = dev.to_np(c)
         assert rel_l2(qkv[s], c_qkv) <= 2e-3, f"qkv s={s}"
-        print(f"config 3 qkv s={s}: rel L2 {rel_l2(qkv[s], c_qkv):.2e}")
+        print(f"FP8 block M=10 qkv s={s}: rel L2 {rel_l2(qkv[s], c_qkv):.2e}")
     for s in (2, 4, 8):
         assert rel_l2(qkv[s], qkv[1]) <= 1e-5, f"qkv split {s} vs unsplit"
-    _silu_teacher_forced(frt, dev, M, 2 * Fm, K, 1, E, "e4m3", o, wu, cu, dec(uc), us, s_y, s_z, "config 3 SiLU")
+    _silu_teacher_forced(frt, dev, M, 2 * Fm, K, 1, E, "e4m3", o, wu, cu, dec(uc), us, s_y, s_z, "FP8 block M=10 SiLU")
     zo = _silu(frt, dev, M, 2 * Fm, K, 1, E, op, wu, cu, s_y, s_z)
     torch.cuda.synchronize()
     zc = dev.operand_codes(zo, E, _mp(M), Fm)
@@ -232,12 +232,12 @@ def test_config3_fp8_static_scale_block(F):
     c_down_p = ref.reduce_partials(ref.gemm_splitk(z_p["deq"], dec(dc), 1), s_z, ds)
     sens_z, sens_d = rel_l2(z_p["deq"], z["deq"]), rel_l2(c_down_p, c_down)
     e2e_z, e2e = rel_l2(dec(zc[:M]), z["deq"]), rel_l2(dev.to_np(c), c_down)
-    print(f"config 3 end to end: SiLU output rel L2 {e2e_z:.2e} (oracle sensitivity {sens_z:.2e}), "
+    print(f"FP8 block M=10 end to end: SiLU output rel L2 {e2e_z:.2e} (oracle sensitivity {sens_z:.2e}), "
           f"down rel L2 {e2e:.2e} (sensitivity {sens_d:.2e})")
-    record("config 3 fp8 end to end", f"SiLU {e2e_z:.2e}, down {e2e:.2e} (bar 2e-3; oracle sensitivity "
+    record("FP8 block M=10 fp8 end to end", f"SiLU {e2e_z:.2e}, down {e2e:.2e} (bar 2e-3; oracle sensitivity "
                                       f"{sens_z:.2e} / {sens_d:.2e})")
-    assert e2e_z <= 2e-3, "config 3 SiLU end to end"
-    assert e2e <= 2e-3, "config 3 down end to end"
+    assert e2e_z <= 2e-3, "FP8 block M=10 SiLU end to end"
+    assert e2e <= 2e-3, "FP8 block M=10 down end to end"
 
     # teacher-forced down projection
     a_pk = dev.to_dev(frt.frt_operand_pack_host(z["codes"], E, M, Fm))
@@ -250,7 +250,7 @@ def test_config3_fp8_static_scale_block(F):
 
 @pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
 @pytest.mark.parametrize("M", [1, 10, 16, 32, 50, 64])
-def test_config5_gate_up_sweep(F, M, dtype):
+def test_gate_up_sweep_k2048_n16384(F, M, dtype):
     frt, dev = F
     w5 = synth.workload5(M)
     K, N, eps = w5["K"], w5["N"], w5["eps"]
@@ -273,7 +273,7 @@ def test_config5_gate_up_sweep(F, M, dtype):
     wc, ws, _ = ref.pack_weight_values(w_v, None, dtype)
     c = ref.reduce_partials(ref.gemm_splitk(o["deq"], codec.decode(wc, dtype), 1), s_y, ws)
     z = ref.silu_gate_quant(c, dtype, s_z)
-    check_codes(dev.operand_codes(op, dt, _mp(M), K)[:M], o["v"], o["mag"], dtype, label=f"config 5 operand M={M}")
+    check_codes(dev.operand_codes(op, dt, _mp(M), K)[:M], o["v"], o["mag"], dtype, label=f"gate|up sweep operand M={M}")
     # the partials of the table's split, reduced on the host in split order, give C
     p = dev.to_np(parts).astype(np.float64)
     got = ref.reduce_partials(p, s_y, ws)
@@ -282,8 +282,8 @@ def test_config5_gate_up_sweep(F, M, dtype):
     zc = dev.operand_codes(zo, dt, _mp(M), N // 2)
     assert np.all(zc[M:] == 0)
     e2e = rel_l2(codec.decode(zc[:M], dtype), z["deq"])
-    assert e2e <= bar, f"config 5 SiLU M={M} end to end"
+    assert e2e <= bar, f"gate|up sweep SiLU M={M} end to end"
     _silu_teacher_forced(frt, dev, M, N, K, 1, dt, dtype, o, wp, cs, codec.decode(wc, dtype), ws, s_y, s_z,
-                         f"config 5 SiLU M={M} {dtype}")
-    print(f"config 5 M={M} {dtype}: split {s_tab}, C rel L2 {rel_l2(got, c):.2e}, SiLU output rel L2 {e2e:.2e}")
-    record(f"config 5 {dtype} M={M}", f"C {rel_l2(got, c):.2e}, SiLU output end to end {e2e:.2e}")
+                         f"gate|up sweep SiLU M={M} {dtype}")
+    print(f"gate|up sweep M={M} {dtype}: split {s_tab}, C rel L2 {rel_l2(got, c):.2e}, SiLU output rel L2 {e2e:.2e}")
+    record(f"gate|up sweep {dtype} M={M}", f"C {rel_l2(got, c):.2e}, SiLU output end to end {e2e:.2e}")
