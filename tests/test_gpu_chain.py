@@ -131,12 +131,14 @@ def test_chain_parity(F, wdtype, M, splits):
 
 @pytest.mark.parametrize("M,prefix,wdtype", [(1, 0, "bf16"), (64, 100, "bf16"), (17, 300, "bf16"), (50, 0, "bf16"),
                                              (1, 0, "e4m3"), (64, 100, "mxfp4"), (17, 300, "e4m3"), (33, 31, "mxfp4"),
-                                             (50, 1100, "bf16"), (10, 900, "e4m3"), (10, 1000, "mxfp4")])
+                                             (50, 1100, "bf16"), (10, 900, "e4m3"), (10, 1000, "mxfp4"),
+                                             (10, 1100, "bf16")])
 def test_chain_edge_shapes(F, M, prefix, wdtype):
     """Smallest and largest action chunks and short prefixes: no prefix (one key chunk,
     the merge kernel not needed), and prefixes that give 2..4 chunks (merge fused into
     the O projection), in bf16, e4m3 and MXFP4 weights; longer prefixes that give 9, 15
-    and 16 key chunks (the fused merge's record slots: one per chunk up to 15, then 16);
+    and 16 key chunks (the fused merge's record slots: one per chunk up to 15, then 16),
+    and 18 chunks (past what the fused merge takes: chunks, a merge kernel, the O GEMM);
     teacher-forced and end to end against the oracle; the production chain (fused,
     read-ahead on) must equal the debug chain bit for bit."""
     frt, chain = F
