@@ -148,7 +148,8 @@ def stand_alone_workloads(torch, frt, device, synth, pool_bytes=1 << 30):
     """The stand-alone workloads as their configurations compose them, each timed with cold
     weights: (1) residual + RMSNorm producer -> bf16 GEMM M=10, K=N=1024, s in {1, 2, 4},
     bf16 output; (2) producer -> gate|up GEMM M=50 (1024 -> 8192) with the SiLU gate ->
-    down projection (4096 -> 1024, fp32 partials), s_down in {1, 2, 4, 8}; (3) the FP8 block
+    down projection (4096 -> 1024, fp32 partials), s_down in {1, 2, 4, 8}, and gate|up split
+    s_up in {2, 4, 8} (SiLU in the consumer) with s_down = 4; (3) the FP8 block
     at M=10: gated residual + AdaRMSNorm -> e4m3, fused QKV (1024 -> 2560, bf16 output),
     gate|up + SiLU gate -> e4m3, down projection (partials).  Static activation scales are
     fixed for timing (their values do not change the work)."""
@@ -198,7 +199,22 @@ def stand_alone_workloads(torch, frt, device, synth, pool_bytes=1 << 30):
         us = time_sequence(torch, enq, ncopy)
         out[f"w2_gated_mlp_m50_bf16_sdown{s_}"] = dict(
             us=round(us, 3), weight_bytes=wbytes, weight_gbs=round(wbytes / (us * 1e-6) / 1e9, 1))
-    del pu, pd
+    # the gate|up GEMM split too: its partials reduced by the consumer kernel, which applies
+    # the SiLU gate and quantises (one kernel more), with the down projection at s = 4
+    parts_up = device.empty_f32(8, M, 2 * Fm)
+    for s_ in (2, 4, 8):
+        def enq(i, st, s_=s_):
+            frt.frt_residual_norm_quant(M, K, x, 1, 1.0, None, r, h, None, None, None, eps, frt.BF16, 1.0, op,
+                                        stream=st)
+            frt.frt_skinny_gemm_splitk(M, 2 * Fm, K, s_, frt.BF16, frt.W_GATE_UP, op, pu[i % ncopy], None, 1.0,
+                                       parts_up, parts_up.numel() * 4, frt.EPI_SILU_GATE_QUANT, z, frt.BF16, 1.0,
+                                       stream=st)
+            frt.frt_skinny_gemm_splitk(M, K, Fm, 4, frt.BF16, frt.W_PLAIN, z, pd[i % ncopy], None, 1.0,
+                                       parts, parts.numel() * 4, frt.EPI_NONE, None, frt.BF16, 1.0, stream=st)
+        us = time_sequence(torch, enq, ncopy)
+        out[f"w2_gated_mlp_m50_bf16_sup{s_}_sdown4"] = dict(
+            us=round(us, 3), weight_bytes=wbytes, weight_gbs=round(wbytes / (us * 1e-6) / 1e9, 1))
+    del pu, pd, parts_up
     # workload 3
     w3 = synth.workload3()
     M, K, Fm, NQ, eps = w3["M"], w3["K"], w3["mlp"], w3["n_qkv"], w3["eps"]
